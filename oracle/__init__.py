@@ -1,0 +1,20 @@
+"""fp64 CPU oracle for DiT attention, int8-QK attention and the first-block-cache reduction.
+
+TEST INFRASTRUCTURE ONLY.  This package is the slow, plain, obviously-correct definition the
+HIP library is checked against.  Only the test suite, the smoke check and the benchmark's CPU
+baseline leg may import or run it; the library and its Python binding never do, and this
+package imports nothing from them (the two share no code; inputs come from ``datagen``).
+
+Modules:
+  attention  -- exact softmax attention (fp64)
+  quant      -- K channel mean, per-block symmetric int8 quantization, quantized attention
+  rel_l1     -- relative L1 distance of two residual tensors
+"""
+from .attention import attention, attention_rows
+from .quant import (k_channel_mean, smooth_k, quantize_blocks, quantize_qk,
+                    attention_int8, dequantize_blocks, Q_BLOCK, K_BLOCK, QMAX)
+from .rel_l1 import rel_l1
+
+__all__ = ["attention", "attention_rows", "k_channel_mean", "smooth_k", "quantize_blocks",
+           "quantize_qk", "attention_int8", "dequantize_blocks", "rel_l1", "Q_BLOCK", "K_BLOCK",
+           "QMAX"]

@@ -1,0 +1,140 @@
+"""int8-QK attention: K smoothing, per-block symmetric int8 quantization, quantized attention.
+
+TEST INFRASTRUCTURE ONLY (see the package docstring).
+
+The pages motivate the method and fix two of its rules:
+
+* 8-bit quantized attention (SageAttention) as a DiT attention backend, with head-level
+  parallelism leaving each device the full sequence -- "TMAP platform image-to-video
+  inference acceleration" page, section on combining with the SageAttention operator; its
+  results section reports attention time cut to one third; the "Diffusion Attention Backends"
+  page lists SAGE_ATTN and warns that its quality must be validated per model.
+* A quantization scale computed from an all-zero group of values is zero, the division by it
+  gives NaN and the output turns black -- same TMAP page, section on operator details; the fix
+  is in the scale logic.  Here: a group whose absolute maximum is 0 gets scale 1.0 (any
+  positive value yields the same all-zero codes, hence the same output).
+
+The rest is this library's stated contract (the pages leave it open):
+
+1. K channel mean over the sequence, per (b, h, d): the exact sum of the bf16 values
+   (math.fsum, correctly rounded to fp64), divided by S in fp64, rounded once to fp32.
+2. Smoothed keys Ks = fp32(K) - mean, one fp32 subtraction.  Subtracting the same vector from
+   every key shifts all scores of a query row by one constant, which the softmax cancels, so
+   the attention output is unchanged; it only shrinks the range the int8 grid must cover.
+   Q is not smoothed and the softmax scale is not folded into the codes.
+3. Blocks: Q in blocks of 128 consecutive tokens, K in blocks of 64, each within one (b, h);
+   a tail block holds only the valid tokens.
+4. Per block: amax = max |x| over the block's tokens and all D channels;
+   scale = amax / 127 as one IEEE fp32 division; amax == 0 gives scale = 1.0.
+5. code = clamp(round_half_even(x / scale), -127, 127), x / scale one IEEE fp32 division.
+6. Attention on the codes: s_ij = (sum_d qc_id * kc_jd) * sq[i // 128] * sk[j // 64] * scale,
+   the integer dot product exact; softmax and the product with V (bf16 values) as in exact
+   attention, all in fp64.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+QMAX = 127
+Q_BLOCK = 128
+K_BLOCK = 64
+
+
+def k_channel_mean(k) -> np.ndarray:
+    """Per-(b, h, d) mean of K over the token axis -> float32 [B, H, D] (rule 1).
+
+    k: [B, H, S, D] fp64 holding bf16 values exactly.
+    """
+    k = np.asarray(k, dtype=np.float64)
+    B, H, S, D = k.shape
+    out = np.empty((B, H, D), dtype=np.float32)
+    for b in range(B):
+        for h in range(H):
+            cols = np.ascontiguousarray(k[b, h].T)
+            for d in range(D):
+                out[b, h, d] = np.float32(math.fsum(cols[d].tolist()) / S)
+    return out
+
+
+def smooth_k(k, kmean) -> np.ndarray:
+    """Ks = fp32(K) - mean, in fp32 (rule 2).  k: [B, H, S, D]; kmean: float32 [B, H, D]."""
+    kf = np.asarray(k, dtype=np.float64).astype(np.float32)
+    return kf - np.asarray(kmean, dtype=np.float32)[:, :, None, :]
+
+
+def _block_scale(amax: np.ndarray) -> np.ndarray:
+    amax = np.asarray(amax, dtype=np.float32)
+    scale = amax / np.float32(QMAX)
+    return np.where(amax == 0, np.float32(1.0), scale).astype(np.float32)
+
+
+def quantize_blocks(x, block: int):
+    """Symmetric int8 codes and per-block scales (rules 3-5).
+
+    x: float32 [B, H, S, D].  Returns (codes int8 [B, H, S, D], scales float32 [B, H, nblk])
+    with nblk = ceil(S / block).
+    """
+    x = np.asarray(x, dtype=np.float32)
+    B, H, S, D = x.shape
+    nblk = -(-S // block)
+    scales = np.empty((B, H, nblk), dtype=np.float32)
+    codes = np.empty((B, H, S, D), dtype=np.int8)
+    for t in range(nblk):
+        blk = x[:, :, t * block:min(S, (t + 1) * block)]
+        scale = _block_scale(np.abs(blk).max(axis=(2, 3)))
+        scales[:, :, t] = scale
+        q = np.rint(blk / scale[:, :, None, None])
+        codes[:, :, t * block:min(S, (t + 1) * block)] = np.clip(q, -QMAX, QMAX).astype(np.int8)
+    return codes, scales
+
+
+def dequantize_blocks(codes, scales, block: int) -> np.ndarray:
+    """codes * scale of their block, fp64 [B, H, S, D]."""
+    codes = np.asarray(codes)
+    S = codes.shape[2]
+    per_tok = np.repeat(np.asarray(scales, dtype=np.float64), block, axis=2)[:, :, :S]
+    return codes.astype(np.float64) * per_tok[..., None]
+
+
+def quantize_qk(q, k, kmean=None):
+    """Rules 1-5 applied to Q and K (fp64 arrays holding bf16 values, [B, H, S, D]).
+
+    Returns a dict with k_mean [B,H,D] f32, q_codes, k_codes int8 [B,H,S,D],
+    q_scale f32 [B,H,ceil(S/128)], k_scale f32 [B,H,ceil(S/64)].
+    """
+    q = np.asarray(q, dtype=np.float64)
+    if kmean is None:
+        kmean = k_channel_mean(k)
+    qc, qs = quantize_blocks(q.astype(np.float32), Q_BLOCK)
+    kc, ks = quantize_blocks(smooth_k(k, kmean), K_BLOCK)
+    return {"k_mean": kmean, "q_codes": qc, "q_scale": qs, "k_codes": kc, "k_scale": ks}
+
+
+def attention_int8(q_codes, q_scale, k_codes, k_scale, v, scale: float | None = None,
+                   rows=None, q_block: int = Q_BLOCK, k_block: int = K_BLOCK) -> np.ndarray:
+    """Attention on int8 codes (rule 6), fp64; rows selects query rows (default: all).
+
+    q_codes, k_codes: int8 [B, H, S, D]; q_scale, k_scale: float32 per block; v: [B, H, S, Dv].
+    """
+    q_codes = np.asarray(q_codes)
+    k_codes = np.asarray(k_codes)
+    v = np.asarray(v, dtype=np.float64)
+    B, H, S, D = q_codes.shape
+    if scale is None:
+        scale = 1.0 / np.sqrt(D)
+    rows = np.arange(S) if rows is None else np.asarray(rows)
+    sq_rows = np.asarray(q_scale, dtype=np.float64)[:, :, rows // q_block]
+    sk_cols = np.repeat(np.asarray(k_scale, dtype=np.float64), k_block, axis=2)[:, :, :k_codes.shape[2]]
+    out = np.empty((B, H, rows.size, v.shape[-1]), dtype=np.float64)
+    for b in range(B):
+        for h in range(H):
+            kc = np.ascontiguousarray(k_codes[b, h].astype(np.float64).T)
+            for r0 in range(0, rows.size, 1024):
+                r = rows[r0:r0 + 1024]
+                dots = q_codes[b, h, r].astype(np.float64) @ kc
+                s = dots * sq_rows[b, h, r0:r0 + 1024, None] * sk_cols[b, h][None, :] * scale
+                w = np.exp(s - s.max(axis=1, keepdims=True))
+                out[b, h, r0:r0 + 1024] = (w @ v[b, h]) / w.sum(axis=1, keepdims=True)
+    return out
