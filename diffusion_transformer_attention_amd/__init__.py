@@ -1,0 +1,173 @@
+"""Python binding of libditattn.so, the MI355X (gfx950) DiT attention library.
+
+Argument marshalling only: every step of the computation runs in the library's HIP kernels.
+PyTorch provides device memory and the current stream; tensors are checked for device,
+dtype, contiguity and shape here, the library validates the rest and returns a status that
+is raised as DitAttnError.  There is no fallback: if the library is not built, loading it
+raises.
+
+Entry points (same names as the C ABI in include/ditattn.h):
+
+  attn_fwd_bf16(q, k, v, out=None, scale=None) -> out
+  attn_fwd_int8qk(q, k, v, out=None, scale=None, workspace=None) -> out
+  resid_rel_l1(a, b, out=None, workspace=None) -> out (fp32 device scalar, shape [1])
+
+plus helpers for the int8 workspace (int8qk_workspace, int8qk_views) and the library path.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+import torch  # loaded first: the library then binds to the HIP runtime torch already holds
+
+__all__ = ["attn_fwd_bf16", "attn_fwd_int8qk", "resid_rel_l1", "int8qk_workspace",
+           "int8qk_views", "int8qk_workspace_bytes", "rel_l1_workspace_bytes", "lib",
+           "LIB_PATH", "DitAttnError"]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libditattn.so")
+
+STATUS = {0: "DITATTN_OK", -1: "DITATTN_EINVAL", -2: "DITATTN_EUNSUPPORTED",
+          -3: "DITATTN_EWORKSPACE", -4: "DITATTN_EHIP"}
+
+_lib = None
+
+
+class DitAttnError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"{STATUS.get(status, status)}: {msg}")
+        self.status = status
+
+
+def lib() -> ctypes.CDLL:
+    """Load libditattn.so (once) and declare its signatures."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is not built; run "
+                           "`python -m diffusion_transformer_attention_amd.build`")
+    L = ctypes.CDLL(LIB_PATH)
+    vp, i, f, sz, i64 = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t, ctypes.c_int64
+    L.attn_fwd_bf16.argtypes = [vp, vp, vp, vp, i, i, i, i, f, vp]
+    L.attn_fwd_bf16.restype = i
+    L.attn_int8qk_workspace_bytes.argtypes = [i, i, i, i]
+    L.attn_int8qk_workspace_bytes.restype = sz
+    L.attn_int8qk_workspace_offsets.argtypes = [i, i, i, i, ctypes.POINTER(sz)]
+    L.attn_int8qk_workspace_offsets.restype = sz
+    L.attn_fwd_int8qk.argtypes = [vp, vp, vp, vp, i, i, i, i, f, vp, sz, vp]
+    L.attn_fwd_int8qk.restype = i
+    L.resid_rel_l1_workspace_bytes.argtypes = [i64]
+    L.resid_rel_l1_workspace_bytes.restype = sz
+    L.resid_rel_l1.argtypes = [vp, vp, i64, vp, vp, sz, vp]
+    L.resid_rel_l1.restype = i
+    L.ditattn_status_string.argtypes = [i]
+    L.ditattn_status_string.restype = ctypes.c_char_p
+    _lib = L
+    return L
+
+
+def _check(status: int):
+    if status != 0:
+        raise DitAttnError(status, lib().ditattn_status_string(status).decode())
+
+
+def _stream(t: torch.Tensor):
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else None
+
+
+def _qkv_shape(q, k, v):
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if not t.is_cuda or t.dtype != torch.bfloat16 or not t.is_contiguous() or t.dim() != 4:
+            raise ValueError(f"{name} must be a contiguous 4-D bf16 CUDA tensor [B, H, S, D]")
+    if q.shape != k.shape or q.shape != v.shape:
+        raise ValueError("q, k, v must have the same shape [B, H, S, D]")
+    return tuple(int(x) for x in q.shape)
+
+
+def _out(out, shape, device):
+    if out is None:
+        return torch.empty(shape, dtype=torch.float32, device=device)
+    if out.dtype != torch.float32 or not out.is_contiguous() or tuple(out.shape) != tuple(shape):
+        raise ValueError(f"out must be a contiguous fp32 tensor of shape {tuple(shape)}")
+    return out
+
+
+def attn_fwd_bf16(q, k, v, out=None, scale=None):
+    """Exact attention O = softmax(Q K^T * scale) V; q, k, v bf16 [B,H,S,D] -> fp32 [B,H,S,D]."""
+    B, H, S, D = _qkv_shape(q, k, v)
+    scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    out = _out(out, (B, H, S, D), q.device)
+    _check(lib().attn_fwd_bf16(_ptr(q), _ptr(k), _ptr(v), _ptr(out), B, H, S, D, scale, _stream(q)))
+    return out
+
+
+def int8qk_workspace_bytes(B, H, S, D) -> int:
+    return int(lib().attn_int8qk_workspace_bytes(B, H, S, D))
+
+
+def int8qk_workspace(B, H, S, D, device) -> torch.Tensor:
+    """A uint8 device buffer large enough for attn_fwd_int8qk on this shape."""
+    n = int8qk_workspace_bytes(B, H, S, D)
+    if n == 0:
+        raise DitAttnError(-1, "invalid shape")
+    return torch.empty(n, dtype=torch.uint8, device=device)
+
+
+def int8qk_views(workspace: torch.Tensor, B, H, S, D) -> dict:
+    """Views of the workspace segments: k_mean, q_scale, k_scale, q_codes, k_codes."""
+    off = (ctypes.c_size_t * 6)()
+    total = lib().attn_int8qk_workspace_offsets(B, H, S, D, off)
+    if total == 0 or workspace.numel() < total:
+        raise DitAttnError(-3, "workspace too small for this shape")
+    nqb, nkb = -(-S // 128), -(-S // 64)
+
+    def seg(i, dtype, shape):
+        n = math.prod(shape) * torch.empty((), dtype=dtype).element_size()
+        return workspace[off[i]:off[i] + n].view(dtype).view(shape)
+
+    return {"k_mean": seg(0, torch.float32, (B, H, D)),
+            "q_scale": seg(1, torch.float32, (B, H, nqb)),
+            "k_scale": seg(2, torch.float32, (B, H, nkb)),
+            "q_codes": seg(3, torch.int8, (B, H, S, D)),
+            "k_codes": seg(4, torch.int8, (B, H, S, D))}
+
+
+def attn_fwd_int8qk(q, k, v, out=None, scale=None, workspace=None):
+    """int8-QK attention (K smoothed by its channel mean, per-block int8 Q/K, bf16 PV)."""
+    B, H, S, D = _qkv_shape(q, k, v)
+    scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    out = _out(out, (B, H, S, D), q.device)
+    if workspace is None:
+        workspace = int8qk_workspace(B, H, S, D, q.device)
+    if workspace.dtype != torch.uint8 or not workspace.is_cuda or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous uint8 CUDA tensor")
+    _check(lib().attn_fwd_int8qk(_ptr(q), _ptr(k), _ptr(v), _ptr(out), B, H, S, D, scale,
+                                 _ptr(workspace), workspace.numel(), _stream(q)))
+    return out
+
+
+def rel_l1_workspace_bytes(n: int) -> int:
+    return int(lib().resid_rel_l1_workspace_bytes(n))
+
+
+def resid_rel_l1(a, b, out=None, workspace=None):
+    """sum|a - b| / sum|b| over two equally shaped bf16 CUDA tensors -> fp32 device tensor [1]."""
+    for name, t in (("a", a), ("b", b)):
+        if not t.is_cuda or t.dtype != torch.bfloat16 or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous bf16 CUDA tensor")
+    if a.shape != b.shape:
+        raise ValueError("a and b must have the same shape")
+    n = a.numel()
+    if out is None:
+        out = torch.empty(1, dtype=torch.float32, device=a.device)
+    if workspace is None:
+        workspace = torch.empty(max(rel_l1_workspace_bytes(n), 1), dtype=torch.uint8, device=a.device)
+    _check(lib().resid_rel_l1(_ptr(a), _ptr(b), n, _ptr(out), _ptr(workspace), workspace.numel(),
+                              _stream(a)))
+    return out

@@ -1,0 +1,38 @@
+// Host-side launchers of the gfx950 kernels (internal to the library; the public C ABI is
+// include/ditattn.h).  Each launcher only enqueues work on `stream` and returns the HIP error
+// of the launch.  Shapes are validated by the caller.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace ditattn {
+
+hipError_t launch_attn_bf16(const void* q, const void* k, const void* v, float* o, int B, int H,
+                            int S, int D, float scale, hipStream_t stream);
+
+hipError_t launch_attn_int8(const void* q_codes, const void* k_codes, const void* v, float* o,
+                            const float* q_scale, const float* k_scale, int B, int H, int S,
+                            int D, float scale, hipStream_t stream);
+
+// Number of token chunks the K-mean partial pass splits each (b, h) into.
+int kmean_chunks(int B, int H, int S);
+
+// K channel mean (exact double-double sum, one division, one rounding to fp32).
+// partial: scratch of B*H*kmean_chunks(B,H,S)*D double pairs.
+hipError_t launch_kmean(const void* k, float* k_mean, double* partial, int B, int H, int S, int D,
+                        hipStream_t stream);
+
+// Per-block int8 quantization of Q (128-token blocks) and smoothed K (64-token blocks).
+hipError_t launch_quant_qk(const void* q, const void* k, const float* k_mean, int8_t* q_codes,
+                           int8_t* k_codes, float* q_scale, float* k_scale, int B, int H, int S,
+                           int D, hipStream_t stream);
+
+// Number of partial-sum workgroups the relative-L1 pass uses for n elements.
+int rel_l1_blocks(int64_t n);
+
+hipError_t launch_rel_l1(const void* a, const void* b, int64_t n, float* out, double* partial,
+                         hipStream_t stream);
+
+}  // namespace ditattn

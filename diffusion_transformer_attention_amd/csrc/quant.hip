@@ -1,0 +1,214 @@
+// Prepass of the int8-QK attention for gfx950: K channel mean and per-block int8 codes.
+//
+// 8-bit attention (SageAttention) is the backend the "TMAP image-to-video inference
+// acceleration" page adopts (section on combining with the quantized attention operator);
+// its operator-details section reports that an all-zero group gives a zero scale, a division
+// by zero and NaN outputs, which the scale rule below guards against.
+//
+// Contract implemented here (bit-exact, so the codes can be compared exactly):
+//   k_mean[b,h,d] = fp32( fl64(exact sum_s K[b,h,s,d]) / S )
+//   Ks            = fp32(K) - k_mean                      (one fp32 subtraction)
+//   per block     amax = max |x|; scale = amax / 127 (IEEE fp32 division), 1.0 if amax == 0
+//   code          = clamp(rint(x / scale), -127, 127)    (IEEE division, ties to even)
+// Q blocks are 128 tokens and K blocks 64 tokens of one (b, h); a tail block covers only the
+// valid tokens.  These kernels are bound by HBM bandwidth: every byte is read once (K twice:
+// once for the mean, once for the codes) and every code written once, with 16-byte accesses.
+#include "device_common.h"
+#include "kernels.h"
+
+namespace ditattn {
+
+namespace {
+
+constexpr int kThreads = 256;
+
+// ---- K channel mean: exact double-double partial sums over token chunks ------------------
+template <int D>
+__global__ __launch_bounds__(kThreads) void kmean_partial_kernel(const uint16_t* __restrict__ k,
+                                                                 double* __restrict__ partial,
+                                                                 int S, int nch, int rows_per) {
+  constexpr int TPR = D / 8;             // threads per token row (8 channels each)
+  constexpr int RPP = kThreads / TPR;    // rows per pass
+  __shared__ double red_hi[kThreads][8];
+  __shared__ double red_lo[kThreads][8];
+
+  const int bh = blockIdx.x / nch;
+  const int chunk = blockIdx.x - bh * nch;
+  const int tid = threadIdx.x;
+  const int cg = tid % TPR, rg = tid / TPR;
+  const int r0 = chunk * rows_per;
+  const int r1 = min(S, r0 + rows_per);
+  const uint16_t* kh = k + (size_t)bh * S * D;
+
+  DDSum acc[8];
+  for (int row = r0 + rg; row < r1; row += RPP) {
+    const u32x4 x = *reinterpret_cast<const u32x4*>(kh + (size_t)row * D + cg * 8);
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      acc[2 * w].add((double)bf16lo(x[w]));
+      acc[2 * w + 1].add((double)bf16hi(x[w]));
+    }
+  }
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    red_hi[tid][e] = acc[e].hi;
+    red_lo[tid][e] = acc[e].lo;
+  }
+  __syncthreads();
+  if (tid < D) {
+    const int g = tid / 8, e = tid % 8;
+    DDSum s;
+    for (int r = 0; r < RPP; ++r) s.merge(red_hi[r * TPR + g][e], red_lo[r * TPR + g][e]);
+    double* dst = partial + 2 * (((size_t)bh * nch + chunk) * D + tid);
+    dst[0] = s.hi;
+    dst[1] = s.lo;
+  }
+}
+
+template <int D>
+__global__ __launch_bounds__(128) void kmean_final_kernel(const double* __restrict__ partial,
+                                                          float* __restrict__ k_mean, int S,
+                                                          int nch) {
+  const int bh = blockIdx.x;
+  const int d = threadIdx.x;
+  if (d >= D) return;
+  DDSum s;
+  for (int c = 0; c < nch; ++c) {
+    const double* p = partial + 2 * (((size_t)bh * nch + c) * D + d);
+    s.merge(p[0], p[1]);
+  }
+  // s.hi is the exact channel sum rounded once to fp64
+  k_mean[(size_t)bh * D + d] = (float)(s.hi / (double)S);
+}
+
+// ---- per-block quantization --------------------------------------------------------------
+template <int D, int BT, bool SMOOTH>
+__device__ __forceinline__ void quant_block(const uint16_t* __restrict__ x, const float* __restrict__ mean,
+                                            int8_t* __restrict__ codes, float* __restrict__ scale_out,
+                                            int S, int bh, int blk) {
+  constexpr int CPR = D / 8;                       // 16-byte chunks per token row
+  constexpr int NC = (BT * CPR) / kThreads;        // chunks per thread
+  static_assert(NC >= 1 && (BT * CPR) % kThreads == 0, "block shape");
+  __shared__ float wmax[kThreads / 64];
+
+  const int tid = threadIdx.x;
+  const int t0 = blk * BT;
+  const int nt = min(BT, S - t0);
+  const size_t base = ((size_t)bh * S + t0) * D;
+
+  float v[NC][8];
+  float amax = 0.f;
+#pragma unroll
+  for (int r = 0; r < NC; ++r) {
+    const int id = tid + r * kThreads;
+    const int tok = id / CPR, ch = id % CPR;
+    u32x4 w = u32x4{0u, 0u, 0u, 0u};
+    if (tok < nt) w = *reinterpret_cast<const u32x4*>(x + base + (size_t)tok * D + ch * 8);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      v[r][2 * e] = bf16lo(w[e]);
+      v[r][2 * e + 1] = bf16hi(w[e]);
+    }
+    if constexpr (SMOOTH) {
+      const f32x4 m0 = *reinterpret_cast<const f32x4*>(mean + (size_t)bh * D + ch * 8);
+      const f32x4 m1 = *reinterpret_cast<const f32x4*>(mean + (size_t)bh * D + ch * 8 + 4);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        v[r][e] = v[r][e] - m0[e];
+        v[r][4 + e] = v[r][4 + e] - m1[e];
+      }
+    }
+    if (tok < nt) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(v[r][e]));
+    }
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off, 64));
+  if ((tid & 63) == 0) wmax[tid >> 6] = amax;
+  __syncthreads();
+  amax = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
+  const float scale = (amax == 0.f) ? 1.0f : amax / 127.0f;
+  if (tid == 0) *scale_out = scale;
+
+#pragma unroll
+  for (int r = 0; r < NC; ++r) {
+    const int id = tid + r * kThreads;
+    const int tok = id / CPR, ch = id % CPR;
+    if (tok >= nt) continue;
+    uint32_t packed[2] = {0u, 0u};
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      float qv = rintf(v[r][e] / scale);
+      qv = fminf(fmaxf(qv, -127.f), 127.f);
+      packed[e >> 2] |= ((uint32_t)(uint8_t)(int8_t)(int)qv) << (8 * (e & 3));
+    }
+    *reinterpret_cast<u32x2*>(codes + base + (size_t)tok * D + ch * 8) = u32x2{packed[0], packed[1]};
+  }
+}
+
+template <int D>
+__global__ __launch_bounds__(kThreads) void quant_qk_kernel(const uint16_t* __restrict__ q,
+                                                            const uint16_t* __restrict__ k,
+                                                            const float* __restrict__ k_mean,
+                                                            int8_t* __restrict__ q_codes,
+                                                            int8_t* __restrict__ k_codes,
+                                                            float* __restrict__ q_scale,
+                                                            float* __restrict__ k_scale, int S,
+                                                            int BH, int nqb, int nkb) {
+  const int id = blockIdx.x;
+  if (id < BH * nqb) {
+    const int bh = id / nqb, blk = id - bh * nqb;
+    quant_block<D, 128, false>(q, nullptr, q_codes, q_scale + (size_t)bh * nqb + blk, S, bh, blk);
+  } else {
+    const int j = id - BH * nqb;
+    const int bh = j / nkb, blk = j - bh * nkb;
+    quant_block<D, 64, true>(k, k_mean, k_codes, k_scale + (size_t)bh * nkb + blk, S, bh, blk);
+  }
+}
+
+}  // namespace
+
+int kmean_chunks(int B, int H, int S) {
+  const long long bh = (long long)B * H;
+  long long by_rows = (S + 127) / 128;
+  long long by_grid = (2048 + bh - 1) / bh;
+  long long n = by_rows < by_grid ? by_rows : by_grid;
+  return (int)(n < 1 ? 1 : n);
+}
+
+hipError_t launch_kmean(const void* k, float* k_mean, double* partial, int B, int H, int S, int D,
+                        hipStream_t stream) {
+  const int nch = kmean_chunks(B, H, S);
+  const int rows_per = (S + nch - 1) / nch;
+  const unsigned bh = (unsigned)(B * H);
+  if (D == 64) {
+    hipLaunchKernelGGL(kmean_partial_kernel<64>, dim3(bh * nch), dim3(kThreads), 0, stream,
+                       static_cast<const uint16_t*>(k), partial, S, nch, rows_per);
+    hipLaunchKernelGGL(kmean_final_kernel<64>, dim3(bh), dim3(128), 0, stream, partial, k_mean, S, nch);
+  } else {
+    hipLaunchKernelGGL(kmean_partial_kernel<128>, dim3(bh * nch), dim3(kThreads), 0, stream,
+                       static_cast<const uint16_t*>(k), partial, S, nch, rows_per);
+    hipLaunchKernelGGL(kmean_final_kernel<128>, dim3(bh), dim3(128), 0, stream, partial, k_mean, S, nch);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_quant_qk(const void* q, const void* k, const float* k_mean, int8_t* q_codes,
+                           int8_t* k_codes, float* q_scale, float* k_scale, int B, int H, int S,
+                           int D, hipStream_t stream) {
+  const int BH = B * H;
+  const int nqb = (S + 127) / 128, nkb = (S + 63) / 64;
+  const dim3 grid((unsigned)((long long)BH * (nqb + nkb)));
+  if (D == 64)
+    hipLaunchKernelGGL(quant_qk_kernel<64>, grid, dim3(kThreads), 0, stream,
+                       static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k), k_mean,
+                       q_codes, k_codes, q_scale, k_scale, S, BH, nqb, nkb);
+  else
+    hipLaunchKernelGGL(quant_qk_kernel<128>, grid, dim3(kThreads), 0, stream,
+                       static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k), k_mean,
+                       q_codes, k_codes, q_scale, k_scale, S, BH, nqb, nkb);
+  return hipGetLastError();
+}
+
+}  // namespace ditattn

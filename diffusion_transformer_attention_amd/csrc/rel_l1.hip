@@ -1,0 +1,123 @@
+// Relative L1 distance of two bf16 residual tensors for gfx950: sum|a - b| / sum|b|.
+//
+// First Block Cache ("ParaAttention" page, First Block Cache section) skips the remaining
+// transformer blocks of a denoising step when the first block's residual differs little from
+// the previous step's; this is the difference it compares with its threshold.  The pass is
+// bound by HBM bandwidth (4 bytes read per element, ~3 flops): a grid-stride stream of
+// 16-byte nontemporal loads with four independent iterations in flight per thread, fp32
+// per-thread sums, an fp64 reduction per workgroup, and a one-workgroup fp64 finish in a
+// fixed order (no atomics, so the result is deterministic).
+#include "device_common.h"
+#include "kernels.h"
+
+namespace ditattn {
+
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kUnroll = 4;
+constexpr int kMaxBlocks = 2048;
+
+__device__ __forceinline__ void accum8(const u32x4& a, const u32x4& b, float& num, float& den) {
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    const float a0 = bf16lo(a[w]), a1 = bf16hi(a[w]);
+    const float b0 = bf16lo(b[w]), b1 = bf16hi(b[w]);
+    num += fabsf(a0 - b0) + fabsf(a1 - b1);
+    den += fabsf(b0) + fabsf(b1);
+  }
+}
+
+__device__ __forceinline__ void block_reduce2(double& x, double& y) {
+  __shared__ double sx[kThreads / 64], sy[kThreads / 64];
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    x += __shfl_xor(x, off, 64);
+    y += __shfl_xor(y, off, 64);
+  }
+  const int tid = threadIdx.x;
+  if ((tid & 63) == 0) {
+    sx[tid >> 6] = x;
+    sy[tid >> 6] = y;
+  }
+  __syncthreads();
+  x = ((sx[0] + sx[1]) + sx[2]) + sx[3];
+  y = ((sy[0] + sy[1]) + sy[2]) + sy[3];
+}
+
+__global__ __launch_bounds__(kThreads) void rel_l1_partial_kernel(const uint16_t* __restrict__ a,
+                                                                  const uint16_t* __restrict__ b,
+                                                                  int64_t n, double* __restrict__ partial) {
+  const int64_t n8 = n >> 3;  // whole 16-byte chunks
+  const u32x4* a8 = reinterpret_cast<const u32x4*>(a);
+  const u32x4* b8 = reinterpret_cast<const u32x4*>(b);
+  const int64_t stride = (int64_t)gridDim.x * kThreads;
+  int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  float num = 0.f, den = 0.f;
+
+  for (; i + (kUnroll - 1) * stride < n8; i += kUnroll * stride) {
+    u32x4 va[kUnroll], vb[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      va[u] = __builtin_nontemporal_load(a8 + i + u * stride);
+      vb[u] = __builtin_nontemporal_load(b8 + i + u * stride);
+    }
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) accum8(va[u], vb[u], num, den);
+  }
+  for (; i < n8; i += stride) accum8(__builtin_nontemporal_load(a8 + i), __builtin_nontemporal_load(b8 + i), num, den);
+
+  // the last n % 8 elements
+  if (blockIdx.x == 0 && threadIdx.x < (n & 7)) {
+    const int64_t e = (n8 << 3) + threadIdx.x;
+    const float av = bf16lo(a[e]), bv = bf16lo(b[e]);
+    num += fabsf(av - bv);
+    den += fabsf(bv);
+  }
+
+  double x = num, y = den;
+  block_reduce2(x, y);
+  if (threadIdx.x == 0) {
+    partial[2 * blockIdx.x] = x;
+    partial[2 * blockIdx.x + 1] = y;
+  }
+}
+
+__global__ __launch_bounds__(kThreads) void rel_l1_final_kernel(const double* __restrict__ partial,
+                                                                int nblocks, float* __restrict__ out) {
+  double x = 0.0, y = 0.0;
+  for (int j = threadIdx.x; j < nblocks; j += kThreads) {
+    x += partial[2 * j];
+    y += partial[2 * j + 1];
+  }
+  block_reduce2(x, y);
+  if (threadIdx.x == 0) {
+    float r;
+    if (y == 0.0)
+      r = (x == 0.0) ? 0.f : INFINITY;
+    else
+      r = (float)(x / y);
+    out[0] = r;
+  }
+}
+
+}  // namespace
+
+int rel_l1_blocks(int64_t n) {
+  const int64_t n8 = n >> 3;
+  int64_t nb = (n8 + (int64_t)kThreads * kUnroll - 1) / ((int64_t)kThreads * kUnroll);
+  if (nb < 1) nb = 1;
+  if (nb > kMaxBlocks) nb = kMaxBlocks;
+  return (int)nb;
+}
+
+hipError_t launch_rel_l1(const void* a, const void* b, int64_t n, float* out, double* partial,
+                         hipStream_t stream) {
+  const int nb = rel_l1_blocks(n);
+  hipLaunchKernelGGL(rel_l1_partial_kernel, dim3(nb), dim3(kThreads), 0, stream,
+                     static_cast<const uint16_t*>(a), static_cast<const uint16_t*>(b), n, partial);
+  hipLaunchKernelGGL(rel_l1_final_kernel, dim3(1), dim3(kThreads), 0, stream, partial, nb, out);
+  return hipGetLastError();
+}
+
+}  // namespace ditattn

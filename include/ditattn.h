@@ -1,0 +1,126 @@
+/*
+ * ditattn.h -- C ABI of the DiT attention library for AMD Instinct MI355X (gfx950).
+ *
+ * Three operations, all non-causal and all on one GPU:
+ *
+ *   attn_fwd_bf16    O = softmax(Q K^T * scale) V per (batch, head), QK^T and PV on bf16
+ *                    matrix cores.  The DiT self-attention that the "Diffusion Attention
+ *                    Backends" page (vLLM-Omni, Overview and Backend Options) dispatches to
+ *                    FlashAttention / scaled_dot_product_attention, computed blockwise
+ *                    on chip as the "Flash Attention 2 for Z-Image S3-DiT" page (hotdry blog,
+ *                    method paragraph) describes; the flash-attention op is 73.76% of a video
+ *                    DiT's FLOPs in the FLOP table of the "TMAP image-to-video inference
+ *                    acceleration" page (section on overlapping communication).
+ *   attn_fwd_int8qk  The same attention with Q and K quantized to int8 (8-bit attention as in
+ *                    the TMAP page's SageAttention section and the SAGE_ATTN backend), with the
+ *                    zero-scale guard of the TMAP page's operator-details section; PV stays
+ *                    bf16.
+ *   resid_rel_l1     sum|a - b| / sum|b| over two residual tensors: the first-block residual
+ *                    difference that First Block Cache compares with its threshold
+ *                    ("ParaAttention" page, First Block Cache section).
+ *
+ * Conventions shared by every call:
+ *   - Tensor pointers are DEVICE pointers, allocated and owned by the caller.  The library
+ *     allocates no memory and keeps no state between calls.
+ *   - Every tensor is contiguous, row-major, and 16-byte aligned.
+ *   - Attention tensors are [B, H, S, D]: batch, head, token, channel (channel fastest).
+ *     Q, K, V are bf16 (raw 16-bit patterns); O is fp32.
+ *   - `stream` is a hipStream_t (NULL = the default stream).  Each call only enqueues work on
+ *     it and returns; results are valid once the caller synchronises with the stream.
+ *   - Return value: DITATTN_OK (0) or a negative status.  Arguments are validated before any
+ *     work is enqueued, so on DITATTN_EINVAL / EUNSUPPORTED / EWORKSPACE nothing was launched
+ *     and no HIP call was made.  DITATTN_EHIP means the HIP runtime rejected a launch.
+ *   - Inputs are assumed finite; NaN or Inf inputs give unspecified outputs.
+ *   - Calls are thread-safe and re-entrant; concurrent calls that share a workspace or an
+ *     output buffer race.
+ */
+#ifndef DITATTN_H
+#define DITATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#if defined(__GNUC__) || defined(__clang__)
+#define DITATTN_API __attribute__((visibility("default")))
+#else
+#define DITATTN_API
+#endif
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum ditattn_status {
+  DITATTN_OK = 0,
+  DITATTN_EINVAL = -1,       /* null or misaligned pointer, size < 1, scale not finite > 0 */
+  DITATTN_EUNSUPPORTED = -2, /* head dim D other than 64 or 128 */
+  DITATTN_EWORKSPACE = -3,   /* workspace NULL or smaller than the *_workspace_bytes value */
+  DITATTN_EHIP = -4          /* the HIP runtime reported an error for a launch */
+};
+
+/* Exact attention, bf16 in / fp32 out.
+ *   q, k, v : bf16 [B, H, S, D] device pointers (read only)
+ *   o       : fp32 [B, H, S, D] device pointer (written; must not alias q, k, v)
+ *   B, H, S : >= 1;  D : 64 or 128
+ *   scale   : finite and > 0; callers pass 1/sqrt(D), the scaled_dot_product_attention default
+ * o[b,h,i,:] = sum_j softmax_j(scale * q[b,h,i,:] . k[b,h,j,:]) * v[b,h,j,:], all j < S.
+ * Accumulation is fp32; the softmax weights are rounded to bf16 for the PV product. */
+DITATTN_API int attn_fwd_bf16(const void* q, const void* k, const void* v, float* o,
+                  int B, int H, int S, int D, float scale, void* stream);
+
+/* Workspace of attn_fwd_int8qk, in bytes, for the given shape (0 if the shape is invalid).
+ * Layout, each segment starting on a 256-byte boundary, in this order:
+ *   [0] k_mean  fp32 [B, H, D]            per-channel mean of K over the S tokens
+ *   [1] q_scale fp32 [B, H, ceil(S/128)]  one scale per 128-token block of Q
+ *   [2] k_scale fp32 [B, H, ceil(S/64)]   one scale per 64-token block of smoothed K
+ *   [3] q_codes int8 [B, H, S, D]
+ *   [4] k_codes int8 [B, H, S, D]
+ *   [5] scratch  fp64 pairs used while forming k_mean (contents unspecified)
+ * After a successful call segments [0]-[4] hold the values the attention used. */
+DITATTN_API size_t attn_int8qk_workspace_bytes(int B, int H, int S, int D);
+
+/* Byte offsets of the six workspace segments above; returns the total size like
+ * attn_int8qk_workspace_bytes (0 and offsets untouched if the shape is invalid). */
+DITATTN_API size_t attn_int8qk_workspace_offsets(int B, int H, int S, int D, size_t offsets[6]);
+
+/* Attention with int8 Q and K and bf16 PV.
+ *   q, k, v, o, B, H, S, D, scale : as attn_fwd_bf16
+ *   workspace       : device buffer of >= attn_int8qk_workspace_bytes(B, H, S, D) bytes,
+ *                     256-byte aligned, owned by the caller (layout above)
+ * Steps, in stream order:
+ *   1. k_mean[b,h,d] = fp32( fp64(exact sum over s of K[b,h,s,d]) / S ).  The sum is carried
+ *      as an exact double-double, so the result is the correctly rounded fp64 sum, divided in
+ *      fp64 and rounded once to fp32 (exact whenever a channel's values span < 2^100).
+ *   2. Ks = fp32(K) - k_mean (one fp32 subtraction).  Q is not smoothed.
+ *   3. Per block (Q: 128 tokens, K: 64 tokens, within one (b, h); a tail block holds only the
+ *      valid tokens): amax = max|x|, scale = amax / 127 (IEEE fp32 division); amax == 0 gives
+ *      scale = 1.0 so an all-zero block never divides by zero.
+ *      code = clamp(round_half_even(x / scale), -127, 127), x / scale an IEEE fp32 division.
+ *   4. s_ij = (integer dot of the codes) * q_scale * k_scale * scale, online softmax, and
+ *      PV on bf16 matrix cores with fp32 accumulation, o in fp32. */
+DITATTN_API int attn_fwd_int8qk(const void* q, const void* k, const void* v, float* o,
+                    int B, int H, int S, int D, float scale,
+                    void* workspace, size_t workspace_bytes, void* stream);
+
+/* Workspace of resid_rel_l1, in bytes, for n elements (0 if n < 1). */
+DITATTN_API size_t resid_rel_l1_workspace_bytes(int64_t n);
+
+/* Relative L1 distance of two residuals.
+ *   a, b      : bf16 device arrays of n elements each (any shape, flattened), 16-byte aligned
+ *   n         : >= 1
+ *   out       : fp32 device scalar, written with sum|a - b| / sum|b| (b is the reference);
+ *               if sum|b| == 0 it is 0 when the numerator is 0, else +inf
+ *   workspace : device buffer of >= resid_rel_l1_workspace_bytes(n) bytes, caller owned
+ * Per-thread partial sums are fp32, combined in fp64 in a fixed order, so the result is
+ * deterministic for a given n. */
+DITATTN_API int resid_rel_l1(const void* a, const void* b, int64_t n, float* out,
+                 void* workspace, size_t workspace_bytes, void* stream);
+
+/* Static English description of a status code (never NULL). */
+DITATTN_API const char* ditattn_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DITATTN_H */

@@ -1,0 +1,123 @@
+"""The C ABI library: it loads, exports every declared entry point, sizes its workspaces as
+documented, and rejects bad arguments before touching the GPU (no GPU needed)."""
+import ctypes
+import math
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "ditattn.h")
+
+EINVAL, EUNSUP, EWS = -1, -2, -3
+FAKE = 0x100000  # a 256-byte aligned address the library never dereferences on invalid calls
+
+
+@pytest.fixture(scope="module")
+def L():
+    import diffusion_transformer_attention_amd as dta
+    if not os.path.exists(dta.LIB_PATH):
+        from diffusion_transformer_attention_amd.build import build
+        build()
+    return dta.lib()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return re.findall(r"DITATTN_API\s+[\w\s\*]+?\b(\w+)\s*\(", text)
+
+
+def test_header_declares_the_three_calls():
+    names = declared_functions()
+    for n in ("attn_fwd_bf16", "attn_fwd_int8qk", "resid_rel_l1"):
+        assert n in names
+    assert len(names) == 7
+
+
+def test_library_exports_every_declared_symbol(L):
+    for n in declared_functions():
+        assert hasattr(L, n), n
+
+
+def test_status_strings(L):
+    for s in (0, -1, -2, -3, -4, 7):
+        assert L.ditattn_status_string(s)
+
+
+def _align(x, a=256):
+    return (x + a - 1) // a * a
+
+
+@pytest.mark.parametrize("B,H,S,D", [(1, 2, 256, 64), (1, 24, 4608, 128), (2, 24, 11440, 128),
+                                     (1, 24, 118800, 128), (3, 1, 1, 64)])
+def test_int8_workspace_layout(L, B, H, S, D):
+    off = (ctypes.c_size_t * 6)()
+    total = L.attn_int8qk_workspace_offsets(B, H, S, D, off)
+    assert total == L.attn_int8qk_workspace_bytes(B, H, S, D)
+    sizes = [B * H * D * 4, B * H * math.ceil(S / 128) * 4, B * H * math.ceil(S / 64) * 4,
+             B * H * S * D, B * H * S * D]
+    expect = 0
+    for i, sz in enumerate(sizes):
+        assert off[i] == expect and off[i] % 256 == 0
+        expect = _align(expect + sz)
+    assert off[5] == expect and total > off[5] and total % 256 == 0
+
+
+def test_invalid_shapes_give_zero_workspace(L):
+    assert L.attn_int8qk_workspace_bytes(0, 1, 1, 64) == 0
+    assert L.attn_int8qk_workspace_bytes(1, 1, 0, 64) == 0
+    assert L.attn_int8qk_workspace_bytes(1, 1, 8, 96) == 0
+    assert L.resid_rel_l1_workspace_bytes(0) == 0
+    assert L.resid_rel_l1_workspace_bytes(1) >= 16
+    assert L.resid_rel_l1_workspace_bytes(364953600) >= 16
+
+
+def _bf16(L, q=FAKE, k=FAKE + 0x1000, v=FAKE + 0x2000, o=FAKE + 0x3000, B=1, H=1, S=64, D=64,
+          scale=0.125):
+    return L.attn_fwd_bf16(q, k, v, o, B, H, S, D, scale, None)
+
+
+def test_bf16_argument_errors(L):
+    assert _bf16(L, q=None) == EINVAL
+    assert _bf16(L, o=None) == EINVAL
+    assert _bf16(L, k=FAKE + 8) == EINVAL             # misaligned
+    assert _bf16(L, o=FAKE) == EINVAL                 # output aliases q
+    assert _bf16(L, B=0) == EINVAL
+    assert _bf16(L, S=-5) == EINVAL
+    assert _bf16(L, D=96) == EUNSUP
+    assert _bf16(L, D=256) == EUNSUP
+    for bad in (0.0, -1.0, float("inf"), float("nan")):
+        assert _bf16(L, scale=bad) == EINVAL
+    assert _bf16(L, B=1 << 20, H=1 << 10, S=1 << 20) == EINVAL  # grid would overflow
+
+
+def test_int8_argument_errors(L):
+    need = L.attn_int8qk_workspace_bytes(1, 1, 64, 64)
+    args = [FAKE, FAKE + 0x1000, FAKE + 0x2000, FAKE + 0x3000, 1, 1, 64, 64, 0.125]
+    assert L.attn_fwd_int8qk(*args, None, need, None) == EWS
+    assert L.attn_fwd_int8qk(*args, FAKE + 0x8000, need - 1, None) == EWS
+    assert L.attn_fwd_int8qk(*args, FAKE + 0x8010, need, None) == EWS   # not 256-aligned
+    bad = list(args); bad[7] = 80
+    assert L.attn_fwd_int8qk(*bad, FAKE + 0x8000, need, None) == EUNSUP
+    bad = list(args); bad[0] = None
+    assert L.attn_fwd_int8qk(*bad, FAKE + 0x8000, need, None) == EINVAL
+
+
+def test_rel_l1_argument_errors(L):
+    need = L.resid_rel_l1_workspace_bytes(100)
+    assert L.resid_rel_l1(None, FAKE, 100, FAKE + 0x1000, FAKE + 0x2000, need, None) == EINVAL
+    assert L.resid_rel_l1(FAKE, FAKE + 0x100, 0, FAKE + 0x1000, FAKE + 0x2000, need, None) == EINVAL
+    assert L.resid_rel_l1(FAKE + 2, FAKE + 0x100, 100, FAKE + 0x1000, FAKE + 0x2000, need, None) == EINVAL
+    assert L.resid_rel_l1(FAKE, FAKE + 0x100, 100, FAKE + 0x1000, None, need, None) == EWS
+    assert L.resid_rel_l1(FAKE, FAKE + 0x100, 100, FAKE + 0x1000, FAKE + 0x2000, need - 1, None) == EWS
+
+
+def test_binding_rejects_cpu_tensors():
+    import torch
+    import diffusion_transformer_attention_amd as dta
+    x = torch.zeros(1, 1, 8, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        dta.attn_fwd_bf16(x, x, x)
+    with pytest.raises(ValueError):
+        dta.resid_rel_l1(x, x)

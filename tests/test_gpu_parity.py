@@ -1,0 +1,326 @@
+"""GPU parity: the HIP library (through its C ABI) against the fp64 oracle.
+
+Tolerances (floating point, written here):
+  bf16 path       max-abs <= 2e-2 and rel-L2 <= 5e-3 against exact fp64 attention
+  int8-QK path    K mean, Q/K codes and scales bit-exact against the oracle's quantizer;
+                  output rel-L2 <= 1e-2 against the oracle's attention on the same codes
+                  (its deviation from exact attention is printed, not gated)
+  relative L1     |r_gpu - r| <= 1e-4 * r
+rel-L2 = ||x - y||_2 / ||y||_2 over every compared element.  At the largest shapes the
+oracle evaluates sampled query rows (first 64, last 64 and seeded random rows per head);
+output rows are independent, so those rows are exact.
+"""
+import sys
+
+import numpy as np
+import pytest
+
+import datagen
+import oracle
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+if not torch.cuda.is_available():
+    pytest.skip("needs a GPU", allow_module_level=True)
+
+import diffusion_transformer_attention_amd as dta  # noqa: E402
+
+BF16_MAXABS, BF16_RELL2 = 2e-2, 5e-3
+INT8_RELL2 = 1e-2
+RL1_REL = 1e-4
+
+
+def announce(msg):
+    print(f"[gpu-parity] {msg}", file=sys.stderr, flush=True)
+
+
+def dev(bits):
+    """uint16 bf16 bit patterns (numpy) -> bf16 CUDA tensor."""
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).cuda()
+
+
+def rel_l2(x, y):
+    return float(np.linalg.norm((x - y).ravel()) / np.linalg.norm(y.ravel()))
+
+
+def check_bf16(got, ref, what):
+    err = np.abs(got - ref).max()
+    r = rel_l2(got, ref)
+    announce(f"{what}: max-abs {err:.3e} rel-L2 {r:.3e}")
+    assert np.all(np.isfinite(got)), what
+    assert err <= BF16_MAXABS and r <= BF16_RELL2, (what, err, r)
+
+
+def run_bf16(q, k, v, scale=None):
+    out = dta.attn_fwd_bf16(dev(q), dev(k), dev(v), scale=scale)
+    torch.cuda.synchronize()
+    return out
+
+
+def run_int8(q, k, v, scale=None):
+    B, H, S, D = q.shape
+    ws = dta.int8qk_workspace(B, H, S, D, "cuda")
+    out = dta.attn_fwd_int8qk(dev(q), dev(k), dev(v), scale=scale, workspace=ws)
+    torch.cuda.synchronize()
+    views = {n: t.cpu().numpy() for n, t in dta.int8qk_views(ws, B, H, S, D).items()}
+    return out, views
+
+
+def f64(bits):
+    return datagen.bf16_to_f64(bits)
+
+
+# ---------------------------------------------------------------------------------------------
+# bf16 path
+# ---------------------------------------------------------------------------------------------
+
+def test_bf16_tiny_full():
+    announce("attn_fwd_bf16 tiny B1 H2 S256 D64")
+    q, k, v = datagen.attention_inputs("tiny")
+    got = run_bf16(q, k, v).cpu().numpy()
+    check_bf16(got, oracle.attention(f64(q), f64(k), f64(v)), "tiny")
+
+
+@pytest.mark.parametrize("S", [1, 2, 63, 64, 65, 127, 129, 200, 1000])
+@pytest.mark.parametrize("D", [64, 128])
+def test_bf16_ragged_lengths(S, D):
+    announce(f"attn_fwd_bf16 B2 H3 S{S} D{D}")
+    q = datagen.normal_bf16((2, 3, S, D), 100 + D, 0)
+    k = datagen.normal_bf16((2, 3, S, D), 100 + D, 1)
+    v = datagen.normal_bf16((2, 3, S, D), 100 + D, 2)
+    got = run_bf16(q, k, v).cpu().numpy()
+    check_bf16(got, oracle.attention(f64(q), f64(k), f64(v)), f"S={S} D={D}")
+
+
+def test_bf16_invariants_on_gpu():
+    announce("attn_fwd_bf16 invariants B1 H2 S300 D128")
+    S, D = 300, 128
+    q = datagen.normal_bf16((1, 2, S, D), 200, 0)
+    k = datagen.normal_bf16((1, 2, S, D), 200, 1)
+    v = datagen.normal_bf16((1, 2, S, D), 200, 2)
+    # Q = 0 -> every row is the mean of V
+    z = np.zeros_like(q)
+    got = run_bf16(z, k, v).cpu().numpy()
+    mean_v = f64(v).mean(axis=2, keepdims=True)
+    check_bf16(got, np.broadcast_to(mean_v, got.shape), "Q=0 -> mean V")
+    # identical V rows pass through
+    vrow = np.broadcast_to(v[:, :, :1], v.shape).copy()
+    got = run_bf16(q, k, vrow).cpu().numpy()
+    check_bf16(got, np.broadcast_to(f64(v[:, :, :1]), got.shape), "identical V rows")
+    base = run_bf16(q, k, v).cpu().numpy()
+    # joint K/V row permutation
+    perm = np.random.default_rng(0).permutation(S)
+    got = run_bf16(q, k[:, :, perm], v[:, :, perm]).cpu().numpy()
+    check_bf16(got, base.astype(np.float64), "joint K/V permutation")
+    # per-channel K offset (exact in bf16: K on a 1/16 grid, integer offsets)
+    kg = datagen.f64_to_bf16_bits(np.round(f64(k) * 4) / 16)
+    off = np.random.default_rng(1).integers(-3, 4, (1, 2, 1, D)).astype(np.float64)
+    kg_off = datagen.f64_to_bf16_bits(f64(kg) + off)
+    assert np.array_equal(f64(kg_off), f64(kg) + off)
+    a = run_bf16(q, kg, v).cpu().numpy()
+    b = run_bf16(q, kg_off, v).cpu().numpy()
+    check_bf16(b, a.astype(np.float64), "K channel offset")
+    check_bf16(a, oracle.attention(f64(q), f64(kg), f64(v)), "grid K vs oracle")
+
+
+def test_bf16_deterministic():
+    announce("attn_fwd_bf16 determinism image-like B1 H4 S4608 D128")
+    q = datagen.normal_bf16((1, 4, 4608, 128), 300, 0)
+    k = datagen.normal_bf16((1, 4, 4608, 128), 300, 1)
+    v = datagen.normal_bf16((1, 4, 4608, 128), 300, 2)
+    a = run_bf16(q, k, v)
+    b = run_bf16(q, k, v)
+    assert torch.equal(a, b)
+
+
+@pytest.fixture(scope="module")
+def image_inputs():
+    return datagen.attention_inputs("image")
+
+
+def test_bf16_image_full(image_inputs):
+    announce("attn_fwd_bf16 image B1 H24 S4608 D128 (full oracle)")
+    q, k, v = image_inputs
+    got = run_bf16(q, k, v).cpu().numpy()
+    check_bf16(got, oracle.attention(f64(q), f64(k), f64(v)), "image")
+
+
+# ---------------------------------------------------------------------------------------------
+# int8-QK path
+# ---------------------------------------------------------------------------------------------
+
+def check_quant_exact(views, ref, what):
+    for key in ("k_mean", "q_scale", "k_scale"):
+        g, r = views[key], ref[key]
+        assert g.shape == r.shape, (what, key)
+        mism = int(np.sum(g.view(np.uint32) != r.view(np.uint32)))
+        assert mism == 0, f"{what}: {key} differs in {mism} of {r.size} values"
+    for key in ("q_codes", "k_codes"):
+        mism = int(np.sum(views[key] != ref[key]))
+        assert mism == 0, f"{what}: {key} differs in {mism} of {ref[key].size} values"
+    announce(f"{what}: K mean, scales and codes bit-exact")
+
+
+def check_int8_out(got, ref_q, ref_exact, what):
+    r = rel_l2(got, ref_q)
+    dev_exact = rel_l2(got, ref_exact)
+    announce(f"{what}: rel-L2 vs quantized oracle {r:.3e}; vs exact attention {dev_exact:.3e} "
+             f"(max-abs {np.abs(got - ref_exact).max():.3e})")
+    assert np.all(np.isfinite(got)), what
+    assert r <= INT8_RELL2, (what, r)
+
+
+def test_int8_tiny_full():
+    announce("attn_fwd_int8qk tiny B1 H2 S256 D64")
+    q, k, v = datagen.attention_inputs("tiny")
+    out, views = run_int8(q, k, v)
+    ref = oracle.quantize_qk(f64(q), f64(k))
+    check_quant_exact(views, ref, "tiny")
+    oq = oracle.attention_int8(ref["q_codes"], ref["q_scale"], ref["k_codes"], ref["k_scale"], f64(v))
+    check_int8_out(out.cpu().numpy(), oq, oracle.attention(f64(q), f64(k), f64(v)), "tiny")
+
+
+@pytest.mark.parametrize("S,D", [(1, 64), (63, 128), (65, 64), (129, 128), (300, 128), (1000, 64)])
+def test_int8_ragged_lengths(S, D):
+    announce(f"attn_fwd_int8qk B2 H3 S{S} D{D}")
+    q = datagen.normal_bf16((2, 3, S, D), 400 + D, 0)
+    k = datagen.f64_to_bf16_bits(f64(datagen.normal_bf16((2, 3, S, D), 400 + D, 1)) + 1.5)
+    v = datagen.normal_bf16((2, 3, S, D), 400 + D, 2)
+    out, views = run_int8(q, k, v)
+    ref = oracle.quantize_qk(f64(q), f64(k))
+    check_quant_exact(views, ref, f"S={S} D={D}")
+    oq = oracle.attention_int8(ref["q_codes"], ref["q_scale"], ref["k_codes"], ref["k_scale"], f64(v))
+    check_int8_out(out.cpu().numpy(), oq, oracle.attention(f64(q), f64(k), f64(v)), f"S={S} D={D}")
+
+
+def test_int8_zero_scale_guard_cases():
+    S, D = 4608, 128
+    q = datagen.normal_bf16((1, 2, S, D), 500, 0)
+    k = datagen.normal_bf16((1, 2, S, D), 500, 1)
+    v = datagen.normal_bf16((1, 2, S, D), 500, 2)
+    mean_v = f64(v).mean(axis=2, keepdims=True)
+    # (i) Q = 0: every Q block has amax 0
+    announce("attn_fwd_int8qk guard: Q = 0")
+    out, views = run_int8(np.zeros_like(q), k, v)
+    assert np.all(views["q_scale"] == 1.0) and not views["q_codes"].any()
+    got = out.cpu().numpy()
+    check_bf16(got, np.broadcast_to(mean_v, got.shape), "int8 Q=0 -> mean V")
+    # (ii) identical K rows: smoothed K is exactly 0
+    announce("attn_fwd_int8qk guard: identical K rows")
+    kc = np.broadcast_to(k[:, :, 7:8], k.shape).copy()
+    out, views = run_int8(q, kc, v)
+    assert np.all(views["k_scale"] == 1.0) and not views["k_codes"].any()
+    got = out.cpu().numpy()
+    check_bf16(got, np.broadcast_to(mean_v, got.shape), "int8 constant K -> mean V")
+    # (iii) one all-zero Q block (tokens 1280..1407 of head 1) in random Q
+    announce("attn_fwd_int8qk guard: one zero Q block")
+    qz = q.copy()
+    qz[:, 1, 1280:1408] = 0
+    out, views = run_int8(qz, k, v)
+    ref = oracle.quantize_qk(f64(qz), f64(k))
+    check_quant_exact(views, ref, "zero Q block")
+    assert views["q_scale"][0, 1, 10] == 1.0
+    got = out.cpu().numpy()
+    assert np.all(np.isfinite(got))
+    np.testing.assert_allclose(got[0, 1, 1280:1408], np.broadcast_to(mean_v[0, 1], (128, D)),
+                               rtol=0, atol=BF16_MAXABS)
+
+
+def test_int8_image_zero_channel(image_inputs):
+    announce("attn_fwd_int8qk image B1 H24 S4608 D128 with K[:,0,:,0] = 0 (full oracle)")
+    q, k, v = image_inputs
+    k = datagen.with_zero_k_channel(k, 0, 0)
+    out, views = run_int8(q, k, v)
+    ref = oracle.quantize_qk(f64(q), f64(k))
+    check_quant_exact(views, ref, "image int8")
+    assert ref["k_mean"][0, 0, 0] == 0 and not views["k_codes"][0, 0, :, 0].any()
+    oq = oracle.attention_int8(ref["q_codes"], ref["q_scale"], ref["k_codes"], ref["k_scale"], f64(v))
+    check_int8_out(out.cpu().numpy(), oq, oracle.attention(f64(q), f64(k), f64(v)), "image int8")
+
+
+# ---------------------------------------------------------------------------------------------
+# large shapes: sampled rows
+# ---------------------------------------------------------------------------------------------
+
+def sampled_checks(name, n_random):
+    q, k, v = datagen.attention_inputs(name)
+    B, H, S, D = q.shape
+    rows = datagen.sample_rows(S, n_random, seed=77)
+    announce(f"{name}: B{B} H{H} S{S} D{D}, {rows.size} sampled rows per head")
+    qd, kd, vd = dev(q), dev(k), dev(v)
+    ob = dta.attn_fwd_bf16(qd, kd, vd)
+    ws = dta.int8qk_workspace(B, H, S, D, "cuda")
+    oi = dta.attn_fwd_int8qk(qd, kd, vd, workspace=ws)
+    torch.cuda.synchronize()
+    idx = torch.from_numpy(rows).cuda()
+    ob = ob.index_select(2, idx).cpu().numpy()
+    oi = oi.index_select(2, idx).cpu().numpy()
+    views = {n: t.cpu().numpy() for n, t in dta.int8qk_views(ws, B, H, S, D).items()}
+    del qd, kd, vd, ws
+    torch.cuda.empty_cache()
+    ref = oracle.quantize_qk(f64(q), f64(k))
+    check_quant_exact(views, ref, f"{name} int8")
+    exact = np.empty_like(ob, dtype=np.float64)
+    quant = np.empty_like(ob, dtype=np.float64)
+    for b in range(B):
+        for h in range(H):
+            sl = (slice(b, b + 1), slice(h, h + 1))
+            exact[sl] = oracle.attention_rows(f64(q[sl]), f64(k[sl]), f64(v[sl]), rows)
+            quant[sl] = oracle.attention_int8(ref["q_codes"][sl], ref["q_scale"][sl], ref["k_codes"][sl],
+                                              ref["k_scale"][sl], f64(v[sl]), rows=rows)
+    check_bf16(ob, exact, f"{name} bf16 (sampled rows)")
+    check_int8_out(oi, quant, exact, f"{name} int8 (sampled rows)")
+
+
+def test_video_both_paths_sampled():
+    sampled_checks("video", 384)
+
+
+def test_longvideo_both_paths_sampled():
+    sampled_checks("longvideo", 128)
+
+
+# ---------------------------------------------------------------------------------------------
+# relative L1
+# ---------------------------------------------------------------------------------------------
+
+def run_rl1(a, b):
+    r = dta.resid_rel_l1(dev(a), dev(b))
+    torch.cuda.synchronize()
+    return float(r.item())
+
+
+def test_rel_l1_closed_forms():
+    announce("resid_rel_l1 closed forms")
+    b = datagen.normal_bf16((1000, 3), 600, 4)
+    bf = f64(b)
+    two_b = datagen.f64_to_bf16_bits(2 * bf)
+    neg_b = datagen.f64_to_bf16_bits(-bf)
+    zero = np.zeros_like(b)
+    assert run_rl1(b, b) == 0.0
+    assert run_rl1(two_b, b) == 1.0
+    assert run_rl1(neg_b, b) == 2.0
+    assert run_rl1(zero, b) == 1.0
+    assert run_rl1(zero, zero) == 0.0
+    assert run_rl1(b, zero) == float("inf")
+
+
+@pytest.mark.parametrize("n", [1, 7, 8, 9, 1000, 262143, 1000003])
+def test_rel_l1_ragged(n):
+    announce(f"resid_rel_l1 n={n}")
+    a = datagen.normal_bf16((n,), 700, 4)
+    b = datagen.normal_bf16((n,), 700, 5)
+    ref = oracle.rel_l1(f64(a), f64(b))
+    got = run_rl1(a, b)
+    assert abs(got - ref) <= RL1_REL * ref, (got, ref)
+
+
+def test_rel_l1_longvideo_residuals():
+    a, b = datagen.residual_pair(118800, 3072)
+    announce("resid_rel_l1 [118800, 3072] first-block residuals")
+    ref = oracle.rel_l1(f64(a), f64(b))
+    got = run_rl1(a, b)
+    announce(f"rel-L1 gpu {got:.8f} oracle {ref:.8f}")
+    assert abs(got - ref) <= RL1_REL * ref
+    assert abs(run_rl1(a, b) - got) == 0.0  # deterministic
