@@ -1,0 +1,263 @@
+"""Benchmark of the DiT attention hot path on one MI355X.
+
+One step = the whole path once over one batch of resident synthetic input:
+  attn_fwd_bf16    B=1 H=24 S=118800 D=128 (a 720p 129-frame video latent)
+  attn_fwd_int8qk  same tensors (K mean, int8 quantization and int8-QK attention)
+  resid_rel_l1     two bf16 [118800, 3072] first-block residuals
+Throughput counts 4*B*H*S^2*D flops per attention call; `value` is the counted flops of both
+attention calls per step divided by the step time (the rel-L1 pass is inside the step).
+The image-DiT shape (S=4608) is timed after the main loop and reported in `extra`.
+
+Prints ONE JSON line.  Options: --gpus N (only 1: this build runs on one GPU),
+--steps K, --warmup W, --no-cpu-baseline.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0    # MI355X dense bf16 MFMA
+PEAK_INT8_TOPS = 5000.0      # MI355X dense int8 MFMA
+PEAK_HBM_GBS = 8000.0        # MI355X HBM3E
+ATTN_KERNEL = "attn_fwd_kernel<128, false>"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_bf16_longvideo_traffic.json")
+
+
+def attn_flops(B, H, S, D):
+    return 4.0 * B * H * S * S * D
+
+
+def make_inputs(torch, B, H, S, D, seed, koff_var=2.0):
+    """Seeded synthetic Q, K, V on the GPU: N(0,1), K plus a per-(h, d) offset ~ N(0, var)."""
+    g = torch.Generator(device="cuda")
+    g.manual_seed(seed)
+    shape = (B, H, S, D)
+    q = torch.randn(shape, generator=g, device="cuda", dtype=torch.float32).to(torch.bfloat16)
+    off = math.sqrt(koff_var) * torch.randn((1, H, 1, D), generator=g, device="cuda")
+    k = (torch.randn(shape, generator=g, device="cuda") + off).to(torch.bfloat16)
+    v = torch.randn(shape, generator=g, device="cuda", dtype=torch.float32).to(torch.bfloat16)
+    return q, k, v
+
+
+def make_residuals(torch, rows, cols, seed, noise=0.05):
+    g = torch.Generator(device="cuda")
+    g.manual_seed(seed)
+    b = torch.randn((rows, cols), generator=g, device="cuda").to(torch.bfloat16)
+    a = (b.float() + noise * torch.randn((rows, cols), generator=g, device="cuda")).to(torch.bfloat16)
+    return a, b
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for name in ("attn_fwd.hip", "device_common.h"):
+        with open(os.path.join(ROOT, "diffusion_transformer_attention_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic():
+    """HBM bytes per launch of the bf16 attention kernel, from committed rocprofv3 counters,
+    or None if they were taken on a different kernel source."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("kernel_source_sha256_16") != kernel_source_hash():
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(budget_s=15.0):
+    """The fp64 oracle timed on the host cores on a bounded sample of the step's workload:
+    exact attention for a few query rows of one head at S=118800 (all keys), plus the
+    relative-L1 reduction over a slice of the residuals."""
+    import numpy as np
+    import datagen
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover - threadpoolctl missing
+        threads = len(os.sched_getaffinity(0))
+    S, D = 118800, 128
+    wid = datagen.WORKLOADS["longvideo"][0]
+    off = datagen.k_offsets(wid, 1, D, 2.0)
+    q, k, v = datagen.qkv_head(wid, 0, 0, S, D, off[0])
+    qf, kf, vf = (datagen.bf16_to_f64(t)[None, None] for t in (q, k, v))
+    rows, total_rows, t_attn = 32, 0, 0.0
+    while t_attn < budget_s * 0.8:
+        sel = np.arange(total_rows, total_rows + rows) % S
+        t0 = time.perf_counter()
+        oracle.attention_rows(qf, kf, vf, sel)
+        t_attn += time.perf_counter() - t0
+        total_rows += rows
+        rows = min(rows * 2, 4096)
+    tflops = 4.0 * total_rows * S * D / t_attn / 1e12
+    a, b = datagen.residual_pair(4096, 3072)
+    af, bf = datagen.bf16_to_f64(a), datagen.bf16_to_f64(b)
+    t0 = time.perf_counter()
+    oracle.rel_l1(af, bf)
+    t_rl1 = time.perf_counter() - t0
+    return {
+        "value": tflops, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+        "sample": (f"fp64 exact attention (numpy/BLAS) for {total_rows} query rows of one head "
+                   f"at S=118800, D=128 against all keys, {t_attn:.1f} s; rel-L1 over "
+                   f"[4096, 3072] bf16 residuals {4 * 4096 * 3072 / t_rl1 / 1e9:.2f} GB/s"),
+        "full_step_seconds_extrapolated": 2 * attn_flops(1, 24, S, D) / (tflops * 1e12),
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="only run a plain 1 GiB device-to-device copy three times (the "
+                         "reference kernel for scaling HBM byte counters) and exit")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this library runs on one GPU; --gpus {args.gpus} is not supported "
+              "(the attention shards by (batch, head) across GPUs, which is not built here)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import diffusion_transformer_attention_amd as dta
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    dta.lib()  # fail loudly if the HIP library is missing
+
+    if args.copy_probe:
+        src = torch.ones(1 << 29, dtype=torch.int16, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_probe_bytes_read": src.numel() * 2, "copy_probe_bytes_written": dst.numel() * 2}))
+        return
+
+    B, H, S, D = 1, 24, 118800, 128
+    RL1_ROWS, RL1_COLS = 118800, 3072
+    q, k, v = make_inputs(torch, B, H, S, D, seed=4)
+    a, b = make_residuals(torch, RL1_ROWS, RL1_COLS, seed=5)
+    o_bf16 = torch.empty((B, H, S, D), dtype=torch.float32, device="cuda")
+    o_int8 = torch.empty_like(o_bf16)
+    ws8 = dta.int8qk_workspace(B, H, S, D, "cuda")
+    r_out = torch.empty(1, dtype=torch.float32, device="cuda")
+    ws_rl1 = torch.empty(dta.rel_l1_workspace_bytes(a.numel()), dtype=torch.uint8, device="cuda")
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.current_stream()
+    ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
+
+    def step(marks=None):
+        if marks is not None:
+            marks[0].record(stream)
+        dta.attn_fwd_bf16(q, k, v, out=o_bf16)
+        if marks is not None:
+            marks[1].record(stream)
+        dta.attn_fwd_int8qk(q, k, v, out=o_int8, workspace=ws8)
+        if marks is not None:
+            marks[2].record(stream)
+        dta.resid_rel_l1(a, b, out=r_out, workspace=ws_rl1)
+        if marks is not None:
+            marks[3].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    marks = [[ev() for _ in range(4)] for _ in range(args.steps)]
+    t_start = ev()
+    t_end = ev()
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    t_start.record(stream)
+    for i in range(args.steps):
+        step(marks[i])
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms_step = t_start.elapsed_time(t_end) / args.steps
+
+    ms_bf16 = sum(m[0].elapsed_time(m[1]) for m in marks) / args.steps
+    ms_int8 = sum(m[1].elapsed_time(m[2]) for m in marks) / args.steps
+    ms_rl1 = sum(m[2].elapsed_time(m[3]) for m in marks) / args.steps
+    F = attn_flops(B, H, S, D)
+    value = 2 * F / (ms_step * 1e-3) / 1e12
+    bf16_tflops = F / (ms_bf16 * 1e-3) / 1e12
+    int8_tops = F / (ms_int8 * 1e-3) / 1e12
+    rl1_bytes = 4.0 * a.numel()
+    rl1_gbs = rl1_bytes / (ms_rl1 * 1e-3) / 1e9
+
+    # image-DiT shape, timed separately (not part of `value`)
+    qi, ki, vi = make_inputs(torch, 1, 24, 4608, 128, seed=1)
+    ws_i = dta.int8qk_workspace(1, 24, 4608, 128, "cuda")
+    oi = torch.empty((1, 24, 4608, 128), dtype=torch.float32, device="cuda")
+    img = {}
+    for name, fn in (("bf16", lambda: dta.attn_fwd_bf16(qi, ki, vi, out=oi)),
+                     ("int8qk", lambda: dta.attn_fwd_int8qk(qi, ki, vi, out=oi, workspace=ws_i))):
+        for _ in range(5):
+            fn()
+        e0, e1 = ev(), ev()
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(50):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / 50
+        img[name] = {"ms": ms, "tflops": attn_flops(1, 24, 4608, 128) / (ms * 1e-3) / 1e12}
+    img["bf16"]["frac_bf16_peak"] = img["bf16"]["tflops"] / PEAK_BF16_TFLOPS
+    img["int8qk"]["frac_int8_peak"] = img["int8qk"]["tflops"] / PEAK_INT8_TOPS
+
+    traffic = load_traffic()
+    line = {
+        "metric": "DiT attention TFLOP/s + % MFMA peak, bf16 & int8-QK, H=24 D=128, S=4608/118800",
+        "value": value,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "longvideo attention B1 H24 S118800 D128 (bf16 + int8-QK) "
+                               "+ rel-L1 over two bf16 [118800, 3072] residuals",
+                   "B": B, "H": H, "S": S, "D": D, "rel_l1_shape": [RL1_ROWS, RL1_COLS],
+                   "parallelism": "single GPU"},
+        "roofline": {"bound": "mfma", "kernel": ATTN_KERNEL, "achieved": bf16_tflops,
+                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": bf16_tflops / PEAK_BF16_TFLOPS, "traffic": traffic},
+        "extra": {
+            "bf16": {"ms": ms_bf16, "tflops": bf16_tflops, "frac_bf16_peak": bf16_tflops / PEAK_BF16_TFLOPS},
+            "int8qk": {"ms": ms_int8, "tops": int8_tops, "frac_int8_peak": int8_tops / PEAK_INT8_TOPS,
+                       "note": "whole call: K mean + quantization + attention"},
+            "rel_l1": {"ms": ms_rl1, "gbs": rl1_gbs, "frac_hbm_peak": rl1_gbs / PEAK_HBM_GBS},
+            "image_S4608": img,
+            "wall_s_timed": wall,
+        },
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline()
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -2,27 +2,37 @@
 //
 // O = softmax(Q K^T * scale) V, computed blockwise on chip so the S x S score matrix never
 // reaches HBM (the IO-aware tiling of the "Flash Attention 2 for Z-Image S3-DiT" page, method
-// paragraph), with a streaming (online) softmax: a running row maximum m and row sum l,
-// rescaled by 2^(m_old - m_new) whenever a new key tile raises the maximum.  The final
-// division by l makes the result exact attention up to rounding.
+// paragraph), with a streaming (online) softmax: a running row maximum m and row sum l; the
+// output is rescaled by 2^(m_old - m_new) when m moves, and the final division by l makes the
+// result exact attention up to rounding.
 //
-// Work decomposition (one workgroup = 4 wavefronts = 128 query rows of one (b, h)):
+// Work decomposition (one workgroup = 4 wavefronts = 128 query rows of one (b, h); two
+// workgroups share a CU, i.e. two wavefronts per SIMD):
 //   * Each wavefront owns 32 query rows.  Its Q fragment stays in VGPRs for the whole pass
-//     as the B operand of S^T = K Q^T (v_mfma_f32_32x32x16_bf16, or
-//     v_mfma_i32_32x32x32_i8 on the int8 codes).
-//   * Computing S^T instead of S puts one query per lane (lane % 32) in the MFMA result, so
-//     a row's maximum and sum are in-lane reductions plus one exchange with lane ^ 32, and the
-//     per-row rescale of the output is a per-lane scalar.
+//     as the B operand of S^T = K Q^T (v_mfma_f32_32x32x16_bf16, or v_mfma_i32_32x32x32_i8
+//     on the int8 codes).  Computing S^T puts one query per lane (lane % 32) in the result,
+//     so a row's maximum and sum are in-lane reductions plus one exchange with lane ^ 32
+//     (v_permlane32_swap), and rescaling a row of the output is a per-lane scalar.
 //   * The P^T tile left in the accumulator registers is directly the B operand of
-//     O^T += V^T P^T (bf16 MFMA): no LDS round trip for P.  Its key order inside each
-//     16-key step is a fixed permutation, which V^T in LDS is stored in.
-//   * K tiles (64 keys) are staged row-major and V tiles transposed (V^T, channel-major) in
-//     LDS, double-buffered: global loads of tile t+1 are in flight while tile t computes.
-//     16-byte LDS chunks are XOR-swizzled so every 16-lane phase of a ds_read_b128 hits 16
-//     distinct bank groups.
+//     O^T += V^T P^T (bf16 MFMA), no LDS round trip for P.  Inside each 16-key step its key
+//     order is a fixed permutation, and the V^T A operand is read from LDS in that order
+//     with ds_read_b64_tr_b16 (gfx950's transposing LDS read), so V stays row-major in LDS.
+//   * K and V tiles of 64 keys go straight from global memory into LDS with
+//     global_load_lds_dwordx4 (no VGPR staging).  Each wave writes 1 KB contiguously per
+//     instruction, so the XOR swizzle of 16-byte chunks is applied to the *global* address a
+//     lane fetches: LDS slot p holds the chunk that belongs at p in the swizzled layout.  The
+//     swizzles make every 16- and 32-lane phase of the MFMA operand reads conflict-free.
+//   * Software pipeline: K runs two tiles ahead of V.  Iteration j issues the loads of K[j+2]
+//     and V[j+1], computes S[j+1] = K[j+1] Q^T on the matrix cores while the VALU turns S[j]
+//     into P[j], then accumulates O += V[j]^T P[j]; one barrier per iteration.
+//   * Lazy rescale: m only moves when a tile's maximum exceeds it by more than 8 (log2
+//     domain); otherwise weights up to 2^8 are used as they are (bf16 and fp32 hold them with
+//     full relative precision).  On typical data O is rescaled a handful of times per row.
 //   * Workgroup ids are remapped so the workgroups the dispatcher places on one XCD (ids
 //     congruent mod 8) process consecutive query tiles of the same head and share its K/V
 //     stream in that XCD's L2.
+#include <type_traits>
+
 #include "device_common.h"
 #include "kernels.h"
 
@@ -34,41 +44,46 @@ constexpr int kThreads = 256;   // 4 wavefronts
 constexpr int kBQ = 128;        // query rows per workgroup (= int8 Q block)
 constexpr int kBK = 64;         // keys per tile (= int8 K block)
 constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLazy = 8.0f;   // log2-domain headroom before the running max moves
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
 template <int D, bool INT8>
 struct Tile {
-  static constexpr int KROW = INT8 ? D : 2 * D;  // bytes per K row
+  static constexpr int KROW = INT8 ? D : 2 * D;  // bytes per K row in LDS
   static constexpr int KCH = KROW / 16;          // 16-byte chunks per K row
   static constexpr int KRPG = 16 / KCH;          // K rows per 256-byte bank period
-  static constexpr int KBYTES = kBK * KROW;
-  static constexpr int VROW = 2 * kBK;           // bytes per V^T row (one channel, 64 keys)
-  static constexpr int VBYTES = D * VROW;
-  static constexpr int BUF = KBYTES + VBYTES;
-  static constexpr int NKL = kBK * KCH / kThreads;  // 16-byte K loads per thread per tile
-  static constexpr int KG = D / 32;                 // keys per thread in the V transpose
-  static constexpr int VDC = D / 8;                 // 8-channel groups per V row
-  static constexpr int NQF = INT8 ? D / 32 : D / 16;  // 16-byte Q fragments per lane
-  static constexpr int NDB = D / 32;                // 32-channel output blocks
-  static_assert(NKL >= 1 && KCH <= 16, "tile shape");
+  static constexpr int KBYTES = kBK * KROW;      // one K tile
+  static constexpr int VROW = 2 * D;             // bytes per V row
+  static constexpr int VCH = VROW / 16;
+  static constexpr int VBYTES = kBK * VROW;      // one V tile
+  static constexpr int KLD = KBYTES / (16 * kThreads);  // 16-byte loads per thread per K tile
+  static constexpr int VLD = VBYTES / (16 * kThreads);
+  static constexpr int NQF = INT8 ? D / 32 : D / 16;   // 16-byte Q fragments per lane
+  static constexpr int NDB = D / 32;                   // 32-channel output blocks
+  static_assert(KLD >= 1 && VLD >= 1 && KCH <= 16, "tile shape");
 };
 
-// Position of key k (0..63) in a V^T row: inside each 16-key step the keys are ordered
-// {0-3, 8-11, 4-7, 12-15}, the order in which the S^T accumulator of lane half h holds them.
-__device__ __forceinline__ int vpos(int k) {
-  const int g = (k >> 2) & 3;
-  return (k & ~15) | ((g & 1) << 3) | ((g >> 1) << 2) | (k & 3);
-}
-
-// Byte offset of 16-byte chunk `ch` of K row `key` in the swizzled K tile.
+// Swizzled chunk of K row `key`: 16 consecutive rows read at one logical chunk land in 16
+// distinct bank groups.
 template <int D, bool INT8>
-__device__ __forceinline__ int koff(int key, int ch) {
+__device__ __forceinline__ int kswz(int key, int ch) {
   using T = Tile<D, INT8>;
-  return key * T::KROW + ((ch ^ ((key / T::KRPG) % T::KCH)) << 4);
+  return ch ^ ((key / T::KRPG) % T::KCH);
 }
 
-// Byte offset of 16-byte chunk `ch` (0..7) of V^T row `d` in the swizzled V^T tile.
-__device__ __forceinline__ int voff(int d, int ch) {
-  return d * (2 * kBK) + ((ch ^ ((d >> 1) & 7)) << 4);
+// Swizzled chunk of V row `row`.  The transposing reads fetch 4 consecutive rows x 32 bytes per
+// 16 lanes (two 16-lane groups side by side); XORing the chunk with a per-(row mod 4) mask
+// spreads them over distinct bank groups for both 16- and 32-lane phases.
+template <int D>
+__device__ __forceinline__ int vswz(int row, int ch) {
+  if constexpr (D == 128) {
+    return ch ^ ((0xEA40 >> (4 * (row & 3))) & 0xF);  // masks {0, 4, 10, 14}
+  } else {
+    return ch ^ ((row & 2) << 1);  // masks {0, 0, 4, 4}
+  }
 }
 
 template <int D, bool INT8>
@@ -79,7 +94,12 @@ void attn_fwd_kernel(const uint8_t* __restrict__ qp, const uint8_t* __restrict__
                      int S, int n_qt, float c) {
   using T = Tile<D, INT8>;
   constexpr int EB = INT8 ? 1 : 2;  // bytes per Q/K element
-  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * T::BUF];
+  // Four distinct LDS objects, so the compiler can tell the buffer being read from the one an
+  // in-flight global->LDS load is filling and does not wait for that load early.
+  __shared__ __attribute__((aligned(1024))) uint8_t kbuf_0[T::KBYTES];
+  __shared__ __attribute__((aligned(1024))) uint8_t kbuf_1[T::KBYTES];
+  __shared__ __attribute__((aligned(1024))) uint8_t vbuf_0[T::VBYTES];
+  __shared__ __attribute__((aligned(1024))) uint8_t vbuf_1[T::VBYTES];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -101,70 +121,61 @@ void attn_fwd_kernel(const uint8_t* __restrict__ qp, const uint8_t* __restrict__
   const uint8_t* vh = vp + head * 2;
   const int nkt = (S + kBK - 1) / kBK;
 
-  // ---- Q fragment: B operand, lane holds query q, channels [32f + 16hh, +16) bytes ------
+  // ---- Q fragment: B operand; lane holds query q, bytes [32f + 16hh, +16) of its row -------
   const int q = qt * kBQ + wave * 32 + l32;
   u32x4 qf[T::NQF];
   {
     const uint8_t* qrow = qp + (head + (size_t)min(q, S - 1) * D) * EB;
 #pragma unroll
     for (int f = 0; f < T::NQF; ++f) {
-      u32x4 x = *reinterpret_cast<const u32x4*>(qrow + f * 32 + hh * 16);
+      const u32x4 x = *reinterpret_cast<const u32x4*>(qrow + f * 32 + hh * 16);
       qf[f] = (q < S) ? x : u32x4{0u, 0u, 0u, 0u};
     }
   }
-
   float cq = c;
   if constexpr (INT8) cq = q_scale[(size_t)bh * n_qt + qt] * c;
 
-  // ---- staging of one K/V tile: global -> registers -> LDS -------------------------------
-  u32x4 kreg[T::NKL];
-  u32x4 vreg[T::KG];
-  const int vdc = tid % T::VDC;   // this thread's 8-channel group of V
-  const int vkg = tid / T::VDC;   // this thread's group of KG keys
-
-  auto gload = [&](int kt) {
-    const int key0 = kt * kBK;
+  // ---- direct global -> LDS tile loads ------------------------------------------------
+  // Slot p (16 bytes) of a tile is written by lane p % 64 of wave (p / 64) % 4 in instruction
+  // p / 256.  Rows past the end of the sequence are clamped to the last row: their scores are
+  // masked to -inf and their V rows then get weight 0.
+  auto load_k = [&](int kt, uint8_t* dst) {
 #pragma unroll
-    for (int r = 0; r < T::NKL; ++r) {
-      const int id = tid + r * kThreads;
-      const int key = id / T::KCH, ch = id % T::KCH;
-      const int row = key0 + key;
-      kreg[r] = (row < S) ? *reinterpret_cast<const u32x4*>(kh + (size_t)row * T::KROW + ch * 16)
-                          : u32x4{0u, 0u, 0u, 0u};
+    for (int r = 0; r < T::KLD; ++r) {
+      const int p = r * kThreads + tid;
+      const int key = p / T::KCH, pch = p % T::KCH;
+      const int row = min(kt * kBK + key, S - 1);
+      const uint8_t* src = kh + (size_t)row * T::KROW + kswz<D, INT8>(key, pch) * 16;
+      __builtin_amdgcn_global_load_lds(src, (lds_void*)(dst + (r * kThreads + wave * 64) * 16), 16, 0, 0);
     }
+  };
+  auto load_v = [&](int kt, uint8_t* dst) {
 #pragma unroll
-    for (int i = 0; i < T::KG; ++i) {
-      const int row = key0 + vkg * T::KG + i;
-      vreg[i] = (row < S) ? *reinterpret_cast<const u32x4*>(vh + ((size_t)row * D + vdc * 8) * 2)
-                          : u32x4{0u, 0u, 0u, 0u};
+    for (int r = 0; r < T::VLD; ++r) {
+      const int p = r * kThreads + tid;
+      const int key = p / T::VCH, pch = p % T::VCH;
+      const int row = min(kt * kBK + key, S - 1);
+      const uint8_t* src = vh + (size_t)row * T::VROW + vswz<D>(key, pch) * 16;
+      __builtin_amdgcn_global_load_lds(src, (lds_void*)(dst + (r * kThreads + wave * 64) * 16), 16, 0, 0);
     }
   };
 
-  auto lstore = [&](int buf) {
-    uint8_t* sk = smem + buf * T::BUF;
-    uint8_t* sv = sk + T::KBYTES;
+  // ---- per-lane LDS read offsets (loop invariant) --------------------------------------
+  // K (A operand of S^T = K Q^T): lane reads row kb2 * 32 + l32, logical chunk 2f + hh.
+  int koffs[T::NQF];
 #pragma unroll
-    for (int r = 0; r < T::NKL; ++r) {
-      const int id = tid + r * kThreads;
-      const int key = id / T::KCH, ch = id % T::KCH;
-      *reinterpret_cast<u32x4*>(sk + koff<D, INT8>(key, ch)) = kreg[r];
-    }
-    // transpose KG keys x 8 channels into 8 channel rows of KG consecutive positions
-    const int pos = vpos(vkg * T::KG);
+  for (int f = 0; f < T::NQF; ++f) koffs[f] = l32 * T::KROW + kswz<D, INT8>(l32, 2 * f + hh) * 16;
+  // V (A operand of O^T = V^T P^T) via ds_read_b64_tr_b16: 16-lane group g = lane / 16 covers
+  // channels n0 = 32 db + 16 (g % 2) .. +15 and keys 16 c4 + 8 part + 4 hh + 0..3; lane j of
+  // the group addresses row (j / 4) of those four and channels n0 + 4 (j % 4) .. +3.
+  const int gj = lane & 15;
+  const int vrow = 4 * hh + (gj >> 2);
+  int voffs[T::NDB];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int d = vdc * 8 + e;
-      uint32_t w[T::KG];
-#pragma unroll
-      for (int i = 0; i < T::KG; ++i) w[i] = (e & 1) ? (vreg[i][e >> 1] >> 16) : (vreg[i][e >> 1] & 0xFFFFu);
-      const int off = voff(d, pos >> 3) + ((pos & 7) << 1);
-      if constexpr (T::KG == 4) {
-        *reinterpret_cast<u32x2*>(sv + off) = u32x2{w[0] | (w[1] << 16), w[2] | (w[3] << 16)};
-      } else {
-        *reinterpret_cast<uint32_t*>(sv + off) = w[0] | (w[1] << 16);
-      }
-    }
-  };
+  for (int db = 0; db < T::NDB; ++db) {
+    const int col = 32 * db + 16 * ((lane >> 4) & 1) + 4 * (gj & 3);
+    voffs[db] = vrow * T::VROW + vswz<D>(vrow, col >> 3) * 16 + (col & 7) * 2;
+  }
 
   f32x16 oacc[T::NDB];
 #pragma unroll
@@ -172,109 +183,130 @@ void attn_fwd_kernel(const uint8_t* __restrict__ qp, const uint8_t* __restrict__
   float m_run = -INFINITY;  // running max of the scaled (log2-domain) scores of row q
   float l_run = 0.f;        // this lane's share of the running row sum
 
-  gload(0);
-  lstore(0);
-  __syncthreads();
-
-  for (int kt = 0; kt < nkt; ++kt) {
-    const int buf = kt & 1;
-    if (kt + 1 < nkt) gload(kt + 1);
-    const uint8_t* sk = smem + buf * T::BUF;
-    const uint8_t* sv = sk + T::KBYTES;
-
-    // ---- S^T = K Q^T: lane holds keys 32kb + 8j + 4hh + i (register 4j + i), query q ----
-    float s[2][16];
+  // S^T tile of one K buffer: register 16 kb2 + r of lane holds key 32 kb2 + 8 (r / 4) +
+  // 4 hh + r % 4, query q.
+  auto qk = [&](const uint8_t* kbuf, float (&s)[32]) {
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      const int key = kb * 32 + l32;
+    for (int kb2 = 0; kb2 < 2; ++kb2) {
       if constexpr (INT8) {
         i32x16 acc = i32x16{};
 #pragma unroll
         for (int f = 0; f < T::NQF; ++f) {
-          const u32x4 a = *reinterpret_cast<const u32x4*>(sk + koff<D, INT8>(key, 2 * f + hh));
+          const u32x4 a = *reinterpret_cast<const u32x4*>(kbuf + kb2 * 32 * T::KROW + koffs[f]);
           acc = __builtin_amdgcn_mfma_i32_32x32x32_i8(__builtin_bit_cast(i32x4, a),
                                                       __builtin_bit_cast(i32x4, qf[f]), acc, 0, 0, 0);
         }
 #pragma unroll
-        for (int r = 0; r < 16; ++r) s[kb][r] = (float)acc[r];
+        for (int r = 0; r < 16; ++r) s[16 * kb2 + r] = (float)acc[r];
       } else {
         f32x16 acc = f32x16{};
 #pragma unroll
         for (int f = 0; f < T::NQF; ++f) {
-          const u32x4 a = *reinterpret_cast<const u32x4*>(sk + koff<D, INT8>(key, 2 * f + hh));
+          const u32x4 a = *reinterpret_cast<const u32x4*>(kbuf + kb2 * 32 * T::KROW + koffs[f]);
           acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
                                                         __builtin_bit_cast(bf16x8, qf[f]), acc, 0, 0, 0);
         }
 #pragma unroll
-        for (int r = 0; r < 16; ++r) s[kb][r] = acc[r];
+        for (int r = 0; r < 16; ++r) s[16 * kb2 + r] = acc[r];
       }
     }
+  };
 
-    // keys past the end of the sequence get zero weight
-    if (kt == nkt - 1 && (S % kBK) != 0) {
+  // One pipeline stage: softmax of tile j (scores in `s`), S[j+1] into `sn`, O += V[j]^T P[j].
+  auto stage = [&](int j, auto par_c, float (&s)[32], float (&sn)[32]) {
+    constexpr int par = decltype(par_c)::value;
+    uint8_t* const kb_cur = par ? kbuf_1 : kbuf_0;    // held K[j]; receives K[j+2]
+    uint8_t* const kb_next = par ? kbuf_0 : kbuf_1;   // holds K[j+1]
+    uint8_t* const vb_cur = par ? vbuf_1 : vbuf_0;    // holds V[j]
+    uint8_t* const vb_next = par ? vbuf_0 : vbuf_1;   // receives V[j+1]
+    if (j + 2 < nkt) load_k(j + 2, kb_cur);
+    if (j + 1 < nkt) load_v(j + 1, vb_next);
+
+    if (j == nkt - 1 && (S % kBK) != 0) {
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+      for (int r = 0; r < 32; ++r) {
+        const int key = j * kBK + 32 * (r >> 4) + 8 * ((r >> 2) & 3) + 4 * hh + (r & 3);
+        if (key >= S) s[r] = -INFINITY;
+      }
+    }
+    float cf = cq;
+    if constexpr (INT8) cf = cq * k_scale[(size_t)bh * nkt + j];
+    float mx = s[0];
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = kt * kBK + kb * 32 + 8 * (r >> 2) + 4 * hh + (r & 3);
-          if (key >= S) s[kb][r] = -INFINITY;
-        }
+    for (int r = 1; r < 32; ++r) mx = fmaxf(mx, s[r]);
+    mx = xor32_max(mx) * cf;
+    if (__builtin_amdgcn_ballot_w64(mx > m_run + kLazy) != 0) {
+      const float m_new = fmaxf(m_run, mx);
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+      m_run = m_new;
+      l_run *= alpha;
+#pragma unroll
+      for (int db = 0; db < T::NDB; ++db) oacc[db] *= alpha;
     }
 
-    // ---- online softmax in the log2 domain: t = s * cf, p = 2^(t - m) ----------------
-    float cf = cq;
-    if constexpr (INT8) cf = cq * k_scale[(size_t)bh * nkt + kt];
-    float mx = s[0][0];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
-    mx = xor32_max(mx);
-    const float m_new = fmaxf(m_run, mx * cf);
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-    m_run = m_new;
-
+    // S[j+1] on the matrix cores (K[j+1] is resident) while the VALU forms P[j]
+    qk(kb_next, sn);
     bf16x8 pb[4];
-    float psum = 0.f;
 #pragma unroll
     for (int c4 = 0; c4 < 4; ++c4)
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float p = __builtin_amdgcn_exp2f(fmaf(s[c4 >> 1][8 * (c4 & 1) + e], cf, -m_new));
-        psum += p;
-        pb[c4][e] = (__bf16)p;
-      }
-    l_run = fmaf(l_run, alpha, psum);
+      for (int e = 0; e < 8; ++e)
+        pb[c4][e] = (__bf16)__builtin_amdgcn_exp2f(fmaf(s[8 * c4 + e], cf, -m_run));
+    // row sum of the bf16 weights that enter PV, two at a time on the dot unit
+    const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
 #pragma unroll
-    for (int db = 0; db < T::NDB; ++db) oacc[db] *= alpha;
+    for (int c4 = 0; c4 < 4; ++c4)
+#pragma unroll
+      for (int e = 0; e < 8; e += 2)
+        l_run = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pb[c4][e], pb[c4][e + 1]}, ones, l_run, false);
 
-    // ---- O^T += V^T P^T: lane holds channels 32db + 8j + 4hh + i, query q -------------
+    // O^T += V[j]^T P[j]: lane holds channels 32 db + 8 (r / 4) + 4 hh + r % 4, query q
 #pragma unroll
-    for (int db = 0; db < T::NDB; ++db) {
-      const int d = db * 32 + l32;
+    for (int c4 = 0; c4 < 4; ++c4) {
 #pragma unroll
-      for (int c4 = 0; c4 < 4; ++c4) {
-        const u32x4 a = *reinterpret_cast<const u32x4*>(sv + voff(d, 2 * c4 + hh));
+      for (int db = 0; db < T::NDB; ++db) {
+        const uint8_t* base = vb_cur + voffs[db] + 16 * c4 * T::VROW;
+        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(base));
+        const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(base + 8 * T::VROW));
+        const u32x2 lo2 = __builtin_bit_cast(u32x2, lo), hi2 = __builtin_bit_cast(u32x2, hi);
+        const u32x4 a = {lo2[0], lo2[1], hi2[0], hi2[1]};
         oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), pb[c4],
                                                            oacc[db], 0, 0, 0);
       }
     }
-
-    if (kt + 1 < nkt) lstore(buf ^ 1);
+    // the loads into kb_cur / vb_next must land before any wave reads them
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
     __syncthreads();
-  }
+  };
 
-  // ---- epilogue: O = O_acc / l, fp32 -------------------------------------------------------
+  // ---- prologue: K[0], K[1], V[0] resident; S[0] computed ---------------------------------
+  load_k(0, kbuf_0);
+  if (nkt > 1) load_k(1, kbuf_1);
+  load_v(0, vbuf_0);
+  __builtin_amdgcn_s_waitcnt(0x0F70);
+  __syncthreads();
+  float sa[32], sb[32];
+  qk(kbuf_0, sa);
+  __syncthreads();  // every wave has read K[0] before its buffer receives K[2]
+
+  int j = 0;
+  for (; j + 1 < nkt; j += 2) {
+    stage(j, std::integral_constant<int, 0>{}, sa, sb);
+    stage(j + 1, std::integral_constant<int, 1>{}, sb, sa);
+  }
+  if (j < nkt) stage(j, std::integral_constant<int, 0>{}, sa, sb);
+
+  // ---- epilogue: O = O_acc / l, fp32 ---------------------------------------------------
   const float inv = 1.f / xor32_sum(l_run);
   if (q < S) {
     float* orow = op + head + (size_t)q * D;
 #pragma unroll
     for (int db = 0; db < T::NDB; ++db)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        f32x4 o4 = {oacc[db][4 * j] * inv, oacc[db][4 * j + 1] * inv, oacc[db][4 * j + 2] * inv,
-                    oacc[db][4 * j + 3] * inv};
-        *reinterpret_cast<f32x4*>(orow + db * 32 + 8 * j + 4 * hh) = o4;
+      for (int jj = 0; jj < 4; ++jj) {
+        const f32x4 o4 = {oacc[db][4 * jj] * inv, oacc[db][4 * jj + 1] * inv,
+                          oacc[db][4 * jj + 2] * inv, oacc[db][4 * jj + 3] * inv};
+        *reinterpret_cast<f32x4*>(orow + db * 32 + 8 * jj + 4 * hh) = o4;
       }
   }
 }

@@ -7,6 +7,7 @@
 namespace ditattn {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef int i32x16 __attribute__((ext_vector_type(16)));
@@ -26,8 +27,15 @@ __device__ __forceinline__ uint32_t f32_to_bf16_bits(float x) {
 }
 
 // Sum / max of a value held by lane l and lane l ^ 32 of a 64-wide wavefront.
-__device__ __forceinline__ float xor32_max(float x) { return fmaxf(x, __shfl_xor(x, 32, 64)); }
-__device__ __forceinline__ float xor32_sum(float x) { return x + __shfl_xor(x, 32, 64); }
+// v_permlane32_swap(x, x) returns {x, x of lane l ^ 32} in some order on every lane.
+__device__ __forceinline__ float xor32_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float xor32_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
 
 // Knuth's TwoSum: a + b is represented exactly as s + e with s = fl(a + b), for any
 // finite a, b (no ordering precondition).
