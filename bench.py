@@ -116,12 +116,39 @@ def cpu_baseline(budget_s=15.0):
     }
 
 
+def time_image_shape(torch, dta, stream, ev, iters=50):
+    """bf16 and int8-QK attention at B1 H24 S4608 D128 (a 1024x1024 image DiT), ms per call."""
+    B, H, S, D = 1, 24, 4608, 128
+    q, k, v = make_inputs(torch, B, H, S, D, seed=1)
+    ws = dta.int8qk_workspace(B, H, S, D, "cuda")
+    o = torch.empty((B, H, S, D), dtype=torch.float32, device="cuda")
+    out = {}
+    for name, fn in (("bf16", lambda: dta.attn_fwd_bf16(q, k, v, out=o)),
+                     ("int8qk", lambda: dta.attn_fwd_int8qk(q, k, v, out=o, workspace=ws))):
+        for _ in range(5):
+            fn()
+        e0, e1 = ev(), ev()
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(iters):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / iters
+        out[name] = {"ms": ms, "tflops": attn_flops(B, H, S, D) / (ms * 1e-3) / 1e12}
+    out["bf16"]["frac_bf16_peak"] = out["bf16"]["tflops"] / PEAK_BF16_TFLOPS
+    out["int8qk"]["frac_int8_peak"] = out["int8qk"]["tflops"] / PEAK_INT8_TOPS
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--headline-only", action="store_true",
+                    help="skip the extra S=4608 timing (profiling runs: one shape per kernel)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy three times (the "
                          "reference kernel for scaling HBM byte counters) and exit")
@@ -204,25 +231,7 @@ def main():
     rl1_gbs = rl1_bytes / (ms_rl1 * 1e-3) / 1e9
 
     # image-DiT shape, timed separately (not part of `value`)
-    qi, ki, vi = make_inputs(torch, 1, 24, 4608, 128, seed=1)
-    ws_i = dta.int8qk_workspace(1, 24, 4608, 128, "cuda")
-    oi = torch.empty((1, 24, 4608, 128), dtype=torch.float32, device="cuda")
-    img = {}
-    for name, fn in (("bf16", lambda: dta.attn_fwd_bf16(qi, ki, vi, out=oi)),
-                     ("int8qk", lambda: dta.attn_fwd_int8qk(qi, ki, vi, out=oi, workspace=ws_i))):
-        for _ in range(5):
-            fn()
-        e0, e1 = ev(), ev()
-        torch.cuda.synchronize()
-        e0.record(stream)
-        for _ in range(50):
-            fn()
-        e1.record(stream)
-        torch.cuda.synchronize()
-        ms = e0.elapsed_time(e1) / 50
-        img[name] = {"ms": ms, "tflops": attn_flops(1, 24, 4608, 128) / (ms * 1e-3) / 1e12}
-    img["bf16"]["frac_bf16_peak"] = img["bf16"]["tflops"] / PEAK_BF16_TFLOPS
-    img["int8qk"]["frac_int8_peak"] = img["int8qk"]["tflops"] / PEAK_INT8_TOPS
+    img = None if args.headline_only else time_image_shape(torch, dta, stream, ev)
 
     traffic = load_traffic()
     line = {
