@@ -65,20 +65,37 @@ __global__ __launch_bounds__(kThreads) void kmean_partial_kernel(const uint16_t*
   }
 }
 
+// One workgroup per (b, h): 256 / D lanes per channel each merge every (256 / D)-th chunk,
+// then a fixed tree joins the lanes; the exact sum is divided by S in fp64 and rounded once.
 template <int D>
-__global__ __launch_bounds__(128) void kmean_final_kernel(const double* __restrict__ partial,
-                                                          float* __restrict__ k_mean, int S,
-                                                          int nch) {
+__global__ __launch_bounds__(kThreads) void kmean_final_kernel(const double* __restrict__ partial,
+                                                               float* __restrict__ k_mean, int S,
+                                                               int nch) {
+  constexpr int L = kThreads / D;  // lanes per channel
+  __shared__ double sh[kThreads], sl[kThreads];
   const int bh = blockIdx.x;
-  const int d = threadIdx.x;
-  if (d >= D) return;
+  const int tid = threadIdx.x;
+  const int d = tid % D, part = tid / D;
   DDSum s;
-  for (int c = 0; c < nch; ++c) {
+  for (int c = part; c < nch; c += L) {
     const double* p = partial + 2 * (((size_t)bh * nch + c) * D + d);
     s.merge(p[0], p[1]);
   }
-  // s.hi is the exact channel sum rounded once to fp64
-  k_mean[(size_t)bh * D + d] = (float)(s.hi / (double)S);
+  sh[tid] = s.hi;
+  sl[tid] = s.lo;
+  __syncthreads();
+#pragma unroll
+  for (int w = L / 2; w >= 1; w >>= 1) {
+    if (part < w) {
+      DDSum t{sh[tid], sl[tid]};
+      t.merge(sh[tid + w * D], sl[tid + w * D]);
+      sh[tid] = t.hi;
+      sl[tid] = t.lo;
+    }
+    __syncthreads();
+  }
+  // sh[d] is the exact channel sum rounded once to fp64
+  if (part == 0) k_mean[(size_t)bh * D + d] = (float)(sh[d] / (double)S);
 }
 
 // ---- per-block quantization --------------------------------------------------------------
@@ -185,11 +202,11 @@ hipError_t launch_kmean(const void* k, float* k_mean, double* partial, int B, in
   if (D == 64) {
     hipLaunchKernelGGL(kmean_partial_kernel<64>, dim3(bh * nch), dim3(kThreads), 0, stream,
                        static_cast<const uint16_t*>(k), partial, S, nch, rows_per);
-    hipLaunchKernelGGL(kmean_final_kernel<64>, dim3(bh), dim3(128), 0, stream, partial, k_mean, S, nch);
+    hipLaunchKernelGGL(kmean_final_kernel<64>, dim3(bh), dim3(kThreads), 0, stream, partial, k_mean, S, nch);
   } else {
     hipLaunchKernelGGL(kmean_partial_kernel<128>, dim3(bh * nch), dim3(kThreads), 0, stream,
                        static_cast<const uint16_t*>(k), partial, S, nch, rows_per);
-    hipLaunchKernelGGL(kmean_final_kernel<128>, dim3(bh), dim3(128), 0, stream, partial, k_mean, S, nch);
+    hipLaunchKernelGGL(kmean_final_kernel<128>, dim3(bh), dim3(kThreads), 0, stream, partial, k_mean, S, nch);
   }
   return hipGetLastError();
 }

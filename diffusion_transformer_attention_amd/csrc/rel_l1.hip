@@ -3,10 +3,10 @@
 // First Block Cache ("ParaAttention" page, First Block Cache section) skips the remaining
 // transformer blocks of a denoising step when the first block's residual differs little from
 // the previous step's; this is the difference it compares with its threshold.  The pass is
-// bound by HBM bandwidth (4 bytes read per element, ~3 flops): a grid-stride stream of
-// 16-byte nontemporal loads with four independent iterations in flight per thread, fp32
-// per-thread sums, an fp64 reduction per workgroup, and a one-workgroup fp64 finish in a
-// fixed order (no atomics, so the result is deterministic).
+// bound by HBM bandwidth (4 bytes read per element, ~3 flops): each workgroup streams one
+// contiguous range with 16-byte nontemporal loads, eight iterations (256 bytes per thread) in
+// flight, fp32 per-thread sums, an fp64 reduction per workgroup, and a one-workgroup fp64
+// finish in a fixed order (no atomics, so the result is deterministic).
 #include "device_common.h"
 #include "kernels.h"
 
@@ -15,8 +15,8 @@ namespace ditattn {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kUnroll = 4;
-constexpr int kMaxBlocks = 2048;
+constexpr int kUnroll = 8;
+constexpr int kMaxBlocks = 4096;
 
 __device__ __forceinline__ void accum8(const u32x4& a, const u32x4& b, float& num, float& den) {
 #pragma unroll
@@ -51,21 +51,24 @@ __global__ __launch_bounds__(kThreads) void rel_l1_partial_kernel(const uint16_t
   const int64_t n8 = n >> 3;  // whole 16-byte chunks
   const u32x4* a8 = reinterpret_cast<const u32x4*>(a);
   const u32x4* b8 = reinterpret_cast<const u32x4*>(b);
-  const int64_t stride = (int64_t)gridDim.x * kThreads;
-  int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  // each workgroup streams one contiguous range of chunks (long sequential bursts per CU)
+  const int64_t per = (n8 + gridDim.x - 1) / gridDim.x;
+  const int64_t beg = (int64_t)blockIdx.x * per;
+  const int64_t end = beg + per < n8 ? beg + per : n8;
   float num = 0.f, den = 0.f;
-
-  for (; i + (kUnroll - 1) * stride < n8; i += kUnroll * stride) {
+  int64_t i = beg + threadIdx.x;
+  for (; i + (kUnroll - 1) * kThreads < end; i += kUnroll * kThreads) {
     u32x4 va[kUnroll], vb[kUnroll];
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
-      va[u] = __builtin_nontemporal_load(a8 + i + u * stride);
-      vb[u] = __builtin_nontemporal_load(b8 + i + u * stride);
+      va[u] = __builtin_nontemporal_load(a8 + i + u * kThreads);
+      vb[u] = __builtin_nontemporal_load(b8 + i + u * kThreads);
     }
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) accum8(va[u], vb[u], num, den);
   }
-  for (; i < n8; i += stride) accum8(__builtin_nontemporal_load(a8 + i), __builtin_nontemporal_load(b8 + i), num, den);
+  for (; i < end; i += kThreads)
+    accum8(__builtin_nontemporal_load(a8 + i), __builtin_nontemporal_load(b8 + i), num, den);
 
   // the last n % 8 elements
   if (blockIdx.x == 0 && threadIdx.x < (n & 7)) {
