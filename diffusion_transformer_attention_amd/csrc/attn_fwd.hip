@@ -137,26 +137,63 @@ void attn_fwd_kernel(const uint8_t* __restrict__ qp, const uint8_t* __restrict__
 
   // ---- direct global -> LDS tile loads ------------------------------------------------
   // Slot p (16 bytes) of a tile is written by lane p % 64 of wave (p / 64) % 4 in instruction
-  // p / 256.  Rows past the end of the sequence are clamped to the last row: their scores are
-  // masked to -inf and their V rows then get weight 0.
+  // p / 256.  The byte offset each lane fetches from, relative to the tile's first row, is
+  // loop invariant (one VGPR per instruction) and the tile base is wave-uniform, so a load is
+  // one global_load_lds with a scalar base and no vector address arithmetic.  Every tile is
+  // a full 64 rows: a partial last tile is read as the last 64 rows of the sequence instead
+  // (keys it shares with the previous tile are masked to -inf, so they get weight 0), and only
+  // a sequence shorter than one tile clamps its rows to the last one.
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+  uint32_t kofl[T::KLD], vofl[T::VLD];
+#pragma unroll
+  for (int r = 0; r < T::KLD; ++r) {
+    const int p = r * kThreads + tid;
+    const int key = p / T::KCH, pch = p % T::KCH;
+    kofl[r] = key * T::KROW + kswz<D, INT8>(key, pch) * 16;
+  }
+#pragma unroll
+  for (int r = 0; r < T::VLD; ++r) {
+    const int p = r * kThreads + tid;
+    const int key = p / T::VCH, pch = p % T::VCH;
+    vofl[r] = key * T::VROW + vswz<D>(key, pch) * 16;
+  }
+  // first row of tile kt (uniform); S >= kBK whenever more than one tile exists
+  auto tile_row = [&](int kt) { return min(kt * kBK, S - kBK); };
+  // The empty asm keeps each offset a 32-bit value at the load, so the address is selected as
+  // scalar base + 32-bit vector offset (the global "saddr" form) instead of a 64-bit VALU add.
   auto load_k = [&](int kt, uint8_t* dst) {
+    const uint8_t* tb = kh + (size_t)tile_row(kt) * T::KROW;
+#pragma unroll
+    for (int r = 0; r < T::KLD; ++r) {
+      uint32_t off = kofl[r];
+      asm volatile("" : "+v"(off));
+      __builtin_amdgcn_global_load_lds(tb + off, (lds_void*)(dst + (r * kThreads + wave_u * 64) * 16), 16, 0, 0);
+    }
+  };
+  auto load_v = [&](int kt, uint8_t* dst) {
+    const uint8_t* tb = vh + (size_t)tile_row(kt) * T::VROW;
+#pragma unroll
+    for (int r = 0; r < T::VLD; ++r) {
+      uint32_t off = vofl[r];
+      asm volatile("" : "+v"(off));
+      __builtin_amdgcn_global_load_lds(tb + off, (lds_void*)(dst + (r * kThreads + wave_u * 64) * 16), 16, 0, 0);
+    }
+  };
+  // the single tile of a sequence shorter than kBK: rows clamped to S - 1
+  auto load_short = [&](uint8_t* kdst, uint8_t* vdst) {
 #pragma unroll
     for (int r = 0; r < T::KLD; ++r) {
       const int p = r * kThreads + tid;
       const int key = p / T::KCH, pch = p % T::KCH;
-      const int row = min(kt * kBK + key, S - 1);
-      const uint8_t* src = kh + (size_t)row * T::KROW + kswz<D, INT8>(key, pch) * 16;
-      __builtin_amdgcn_global_load_lds(src, (lds_void*)(dst + (r * kThreads + wave * 64) * 16), 16, 0, 0);
+      const uint32_t off = min(key, S - 1) * T::KROW + kswz<D, INT8>(key, pch) * 16;
+      __builtin_amdgcn_global_load_lds(kh + off, (lds_void*)(kdst + (r * kThreads + wave_u * 64) * 16), 16, 0, 0);
     }
-  };
-  auto load_v = [&](int kt, uint8_t* dst) {
 #pragma unroll
     for (int r = 0; r < T::VLD; ++r) {
       const int p = r * kThreads + tid;
       const int key = p / T::VCH, pch = p % T::VCH;
-      const int row = min(kt * kBK + key, S - 1);
-      const uint8_t* src = vh + (size_t)row * T::VROW + vswz<D>(key, pch) * 16;
-      __builtin_amdgcn_global_load_lds(src, (lds_void*)(dst + (r * kThreads + wave * 64) * 16), 16, 0, 0);
+      const uint32_t off = min(key, S - 1) * T::VROW + vswz<D>(key, pch) * 16;
+      __builtin_amdgcn_global_load_lds(vh + off, (lds_void*)(vdst + (r * kThreads + wave_u * 64) * 16), 16, 0, 0);
     }
   };
 
@@ -223,10 +260,16 @@ void attn_fwd_kernel(const uint8_t* __restrict__ qp, const uint8_t* __restrict__
     if (j + 1 < nkt) load_v(j + 1, vb_next);
 
     if (j == nkt - 1 && (S % kBK) != 0) {
+      // keys of this tile outside [j * kBK, S): already seen in tile j - 1, or past the end.
+      // In tile-local key numbers the valid range is [lo, hi); the empty asm keeps the
+      // comparisons inside this rarely taken branch.
+      const int t0 = tile_row(j) > 0 ? tile_row(j) : 0;
+      int lo = j * kBK - t0 - 4 * hh, hi = S - t0 - 4 * hh;
+      asm volatile("" : "+v"(lo), "+v"(hi));
 #pragma unroll
       for (int r = 0; r < 32; ++r) {
-        const int key = j * kBK + 32 * (r >> 4) + 8 * ((r >> 2) & 3) + 4 * hh + (r & 3);
-        if (key >= S) s[r] = -INFINITY;
+        const int kc = 32 * (r >> 4) + 8 * ((r >> 2) & 3) + (r & 3);
+        if (kc < lo || kc >= hi) s[r] = -INFINITY;
       }
     }
     float cf = cq;
@@ -280,9 +323,13 @@ void attn_fwd_kernel(const uint8_t* __restrict__ qp, const uint8_t* __restrict__
   };
 
   // ---- prologue: K[0], K[1], V[0] resident; S[0] computed ---------------------------------
-  load_k(0, kbuf_0);
-  if (nkt > 1) load_k(1, kbuf_1);
-  load_v(0, vbuf_0);
+  if (S < kBK) {
+    load_short(kbuf_0, vbuf_0);
+  } else {
+    load_k(0, kbuf_0);
+    if (nkt > 1) load_k(1, kbuf_1);
+    load_v(0, vbuf_0);
+  }
   __builtin_amdgcn_s_waitcnt(0x0F70);
   __syncthreads();
   float sa[32], sb[32];
