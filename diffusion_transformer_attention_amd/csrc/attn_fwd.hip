@@ -25,6 +25,9 @@
 //   * Software pipeline: K runs two tiles ahead of V.  Iteration j issues the loads of K[j+2]
 //     and V[j+1], computes S[j+1] = K[j+1] Q^T on the matrix cores while the VALU turns S[j]
 //     into P[j], then accumulates O += V[j]^T P[j]; one barrier per iteration.
+//   * int8 scores leave the matrix cores already as fp32: the integer accumulator starts at
+//     the bit pattern of 1.5 * 2^23, so its final bits read as fp32 are 1.5 * 2^23 plus the
+//     score, exactly; the bias folds into the exponent offset (no conversion instructions).
 //   * Lazy rescale: m only moves when a tile's maximum exceeds it by more than 8 (log2
 //     domain); otherwise weights up to 2^8 are used as they are (bf16 and fp32 hold them with
 //     full relative precision).  On typical data O is rescaled a handful of times per row.
@@ -40,18 +43,24 @@ namespace ditattn {
 
 namespace {
 
-constexpr int kThreads = 256;   // 4 wavefronts
-constexpr int kBQ = 128;        // query rows per workgroup (= int8 Q block)
+constexpr int kQBlock = 128;    // int8 Q quantization block (tokens)
 constexpr int kBK = 64;         // keys per tile (= int8 K block)
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLazy = 8.0f;   // log2-domain headroom before the running max moves
+// 1.5 * 2^23: every fp32 in [2^23, 2^24) is an integer and consecutive integers have
+// consecutive bit patterns, so bits(kBiasF) + n read as fp32 is kBiasF + n for |n| < 2^22.
+// An int8 score is at most 127 * 127 * 128 < 2^21 in magnitude, so the int8 QK product
+// accumulated onto bits(kBiasF) converts to fp32 without a conversion instruction.
+constexpr float kBiasF = 12582912.0f;
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
-template <int D, bool INT8>
+template <int D, bool INT8, int NW>
 struct Tile {
+  static constexpr int NT = 64 * NW;             // threads per workgroup
+  static constexpr int BQ = 32 * NW;             // query rows per workgroup
   static constexpr int KROW = INT8 ? D : 2 * D;  // bytes per K row in LDS
   static constexpr int KCH = KROW / 16;          // 16-byte chunks per K row
   static constexpr int KRPG = 16 / KCH;          // K rows per 256-byte bank period
@@ -59,18 +68,20 @@ struct Tile {
   static constexpr int VROW = 2 * D;             // bytes per V row
   static constexpr int VCH = VROW / 16;
   static constexpr int VBYTES = kBK * VROW;      // one V tile
-  static constexpr int KLD = KBYTES / (16 * kThreads);  // 16-byte loads per thread per K tile
-  static constexpr int VLD = VBYTES / (16 * kThreads);
+  static constexpr int KLD = (KBYTES / 16 + NT - 1) / NT;  // 16-byte loads per thread per K tile
+  static constexpr int VLD = (VBYTES / 16 + NT - 1) / NT;
+  static constexpr bool KPART = (KBYTES / 16) % NT != 0;  // last K load only on some threads
+  static_assert((VBYTES / 16) % NT == 0 && (!KPART || KLD == 1), "tile shape");
   static constexpr int NQF = INT8 ? D / 32 : D / 16;   // 16-byte Q fragments per lane
   static constexpr int NDB = D / 32;                   // 32-channel output blocks
-  static_assert(KLD >= 1 && VLD >= 1 && KCH <= 16, "tile shape");
+  static_assert(KCH <= 16, "tile shape");
 };
 
 // Swizzled chunk of K row `key`: 16 consecutive rows read at one logical chunk land in 16
 // distinct bank groups.
 template <int D, bool INT8>
 __device__ __forceinline__ int kswz(int key, int ch) {
-  using T = Tile<D, INT8>;
+  using T = Tile<D, INT8, 4>;
   return ch ^ ((key / T::KRPG) % T::KCH);
 }
 
@@ -86,13 +97,15 @@ __device__ __forceinline__ int vswz(int row, int ch) {
   }
 }
 
-template <int D, bool INT8>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2)))
+template <int D, bool INT8, int NW>
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2)))
 void attn_fwd_kernel(const uint8_t* __restrict__ qp, const uint8_t* __restrict__ kp,
                      const uint8_t* __restrict__ vp, float* __restrict__ op,
                      const float* __restrict__ q_scale, const float* __restrict__ k_scale,
                      int S, int n_qt, float c) {
-  using T = Tile<D, INT8>;
+  using T = Tile<D, INT8, NW>;
+  constexpr int kThreads = T::NT;
+  constexpr int kBQ = T::BQ;
   constexpr int EB = INT8 ? 1 : 2;  // bytes per Q/K element
   // Four distinct LDS objects, so the compiler can tell the buffer being read from the one an
   // in-flight global->LDS load is filling and does not wait for that load early.
@@ -133,7 +146,10 @@ void attn_fwd_kernel(const uint8_t* __restrict__ qp, const uint8_t* __restrict__
     }
   }
   float cq = c;
-  if constexpr (INT8) cq = q_scale[(size_t)bh * n_qt + qt] * c;
+  if constexpr (INT8) {
+    const int nqb = (S + kQBlock - 1) / kQBlock;
+    cq = q_scale[(size_t)bh * nqb + (qt * kBQ + wave * 32) / kQBlock] * c;
+  }
 
   // ---- direct global -> LDS tile loads ------------------------------------------------
   // Slot p (16 bytes) of a tile is written by lane p % 64 of wave (p / 64) % 4 in instruction
@@ -163,6 +179,7 @@ void attn_fwd_kernel(const uint8_t* __restrict__ qp, const uint8_t* __restrict__
   // scalar base + 32-bit vector offset (the global "saddr" form) instead of a 64-bit VALU add.
   auto load_k = [&](int kt, uint8_t* dst) {
     const uint8_t* tb = kh + (size_t)tile_row(kt) * T::KROW;
+    if (T::KPART && wave_u * 64 >= T::KBYTES / 16) return;  // this wave has no K slot
 #pragma unroll
     for (int r = 0; r < T::KLD; ++r) {
       uint32_t off = kofl[r];
@@ -183,6 +200,7 @@ void attn_fwd_kernel(const uint8_t* __restrict__ qp, const uint8_t* __restrict__
   auto load_short = [&](uint8_t* kdst, uint8_t* vdst) {
 #pragma unroll
     for (int r = 0; r < T::KLD; ++r) {
+      if (T::KPART && wave_u * 64 >= T::KBYTES / 16) break;
       const int p = r * kThreads + tid;
       const int key = p / T::KCH, pch = p % T::KCH;
       const uint32_t off = min(key, S - 1) * T::KROW + kswz<D, INT8>(key, pch) * 16;
@@ -220,21 +238,38 @@ void attn_fwd_kernel(const uint8_t* __restrict__ qp, const uint8_t* __restrict__
   float m_run = -INFINITY;  // running max of the scaled (log2-domain) scores of row q
   float l_run = 0.f;        // this lane's share of the running row sum
 
+  i32x16 ibias;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) ibias[r] = (int)__builtin_bit_cast(uint32_t, kBiasF);
+  if constexpr (INT8) asm volatile("" : "+v"(ibias));  // an opaque VGPR tuple, not a splat
+
   // S^T tile of one K buffer: register 16 kb2 + r of lane holds key 32 kb2 + 8 (r / 4) +
-  // 4 hh + r % 4, query q.
+  // 4 hh + r % 4, query q.  The int8 variant holds kBiasF + the integer score.
   auto qk = [&](const uint8_t* kbuf, float (&s)[32]) {
 #pragma unroll
     for (int kb2 = 0; kb2 < 2; ++kb2) {
       if constexpr (INT8) {
-        i32x16 acc = i32x16{};
+        // The accumulator starts at the bit pattern of kBiasF, so it ends as kBiasF + the
+        // integer dot product, which read as fp32 is exactly that sum (see kBiasF)
+        i32x16 acc;
 #pragma unroll
         for (int f = 0; f < T::NQF; ++f) {
           const u32x4 a = *reinterpret_cast<const u32x4*>(kbuf + kb2 * 32 * T::KROW + koffs[f]);
-          acc = __builtin_amdgcn_mfma_i32_32x32x32_i8(__builtin_bit_cast(i32x4, a),
-                                                      __builtin_bit_cast(i32x4, qf[f]), acc, 0, 0, 0);
+          if (f == 0) {
+            // first product reads the bias tuple as C and writes a separate accumulator (the
+            // builtin would copy the tuple first); s_nop 1 covers a VALU-written operand
+            asm volatile("s_nop 1\n\tv_mfma_i32_32x32x32_i8 %0, %1, %2, %3"
+                         : "=&v"(acc) : "v"(a), "v"(qf[f]), "v"(ibias));
+          } else {
+            acc = __builtin_amdgcn_mfma_i32_32x32x32_i8(__builtin_bit_cast(i32x4, a),
+                                                        __builtin_bit_cast(i32x4, qf[f]), acc, 0, 0, 0);
+          }
         }
+        // (bit-cast the whole vector: a bit_cast of one subscripted element is miscompiled
+        // to element 0 by this compiler)
+        const f32x16 accf = __builtin_bit_cast(f32x16, acc);
 #pragma unroll
-        for (int r = 0; r < 16; ++r) s[16 * kb2 + r] = (float)acc[r];
+        for (int r = 0; r < 16; ++r) s[16 * kb2 + r] = accf[r];
       } else {
         f32x16 acc = f32x16{};
 #pragma unroll
@@ -277,7 +312,9 @@ void attn_fwd_kernel(const uint8_t* __restrict__ qp, const uint8_t* __restrict__
     float mx = s[0];
 #pragma unroll
     for (int r = 1; r < 32; ++r) mx = fmaxf(mx, s[r]);
-    mx = xor32_max(mx) * cf;
+    mx = xor32_max(mx);
+    if constexpr (INT8) mx -= kBiasF;  // exact: both are integers below 2^24
+    mx *= cf;
     if (__builtin_amdgcn_ballot_w64(mx > m_run + kLazy) != 0) {
       const float m_new = fmaxf(m_run, mx);
       const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
@@ -287,6 +324,9 @@ void attn_fwd_kernel(const uint8_t* __restrict__ qp, const uint8_t* __restrict__
       for (int db = 0; db < T::NDB; ++db) oacc[db] *= alpha;
     }
 
+    // exponent offset: m_run, plus the bias carried by the int8 scores (cf * kBiasF, rounded
+    // once; its error is far below the int8 quantization error of the scores themselves)
+    const float mb = INT8 ? fmaf(cf, kBiasF, m_run) : m_run;
     // S[j+1] on the matrix cores (K[j+1] is resident) while the VALU forms P[j]
     qk(kb_next, sn);
     bf16x8 pb[4];
@@ -294,7 +334,7 @@ void attn_fwd_kernel(const uint8_t* __restrict__ qp, const uint8_t* __restrict__
     for (int c4 = 0; c4 < 4; ++c4)
 #pragma unroll
       for (int e = 0; e < 8; ++e)
-        pb[c4][e] = (__bf16)__builtin_amdgcn_exp2f(fmaf(s[8 * c4 + e], cf, -m_run));
+        pb[c4][e] = (__bf16)__builtin_amdgcn_exp2f(fmaf(s[8 * c4 + e], cf, -mb));
     // row sum of the bf16 weights that enter PV, two at a time on the dot unit
     const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
 #pragma unroll
@@ -358,12 +398,13 @@ void attn_fwd_kernel(const uint8_t* __restrict__ qp, const uint8_t* __restrict__
   }
 }
 
-template <int D, bool INT8>
+template <int D, bool INT8, int NW>
 hipError_t launch(const void* q, const void* k, const void* v, float* o, const float* qs,
                   const float* ks, int B, int H, int S, float scale, hipStream_t stream) {
-  const int n_qt = (S + kBQ - 1) / kBQ;
+  using T = Tile<D, INT8, NW>;
+  const int n_qt = (S + T::BQ - 1) / T::BQ;
   const long long nwg = (long long)B * H * n_qt;
-  hipLaunchKernelGGL((attn_fwd_kernel<D, INT8>), dim3((unsigned)nwg), dim3(kThreads), 0, stream,
+  hipLaunchKernelGGL((attn_fwd_kernel<D, INT8, NW>), dim3((unsigned)nwg), dim3(T::NT), 0, stream,
                      static_cast<const uint8_t*>(q), static_cast<const uint8_t*>(k),
                      static_cast<const uint8_t*>(v), o, qs, ks, S, n_qt, scale * kLog2e);
   return hipGetLastError();
@@ -371,18 +412,21 @@ hipError_t launch(const void* q, const void* k, const void* v, float* o, const f
 
 }  // namespace
 
+// Waves per workgroup.  Eight-wave workgroups (256 query rows, one per CU) halve the K/V
+// traffic from L2 but measured no faster than four-wave ones (two per CU) on either variant.
+constexpr int kWaves = 4;
 hipError_t launch_attn_bf16(const void* q, const void* k, const void* v, float* o, int B, int H,
                             int S, int D, float scale, hipStream_t stream) {
-  if (D == 64) return launch<64, false>(q, k, v, o, nullptr, nullptr, B, H, S, scale, stream);
-  return launch<128, false>(q, k, v, o, nullptr, nullptr, B, H, S, scale, stream);
+  if (D == 64) return launch<64, false, kWaves>(q, k, v, o, nullptr, nullptr, B, H, S, scale, stream);
+  return launch<128, false, kWaves>(q, k, v, o, nullptr, nullptr, B, H, S, scale, stream);
 }
 
 hipError_t launch_attn_int8(const void* q_codes, const void* k_codes, const void* v, float* o,
                             const float* q_scale, const float* k_scale, int B, int H, int S,
                             int D, float scale, hipStream_t stream) {
   if (D == 64)
-    return launch<64, true>(q_codes, k_codes, v, o, q_scale, k_scale, B, H, S, scale, stream);
-  return launch<128, true>(q_codes, k_codes, v, o, q_scale, k_scale, B, H, S, scale, stream);
+    return launch<64, true, kWaves>(q_codes, k_codes, v, o, q_scale, k_scale, B, H, S, scale, stream);
+  return launch<128, true, kWaves>(q_codes, k_codes, v, o, q_scale, k_scale, B, H, S, scale, stream);
 }
 
 }  // namespace ditattn
