@@ -27,7 +27,7 @@ sys.path.insert(0, ROOT)
 PEAK_BF16_TFLOPS = 2500.0    # MI355X dense bf16 MFMA
 PEAK_INT8_TOPS = 5000.0      # MI355X dense int8 MFMA
 PEAK_HBM_GBS = 8000.0        # MI355X HBM3E
-ATTN_KERNEL = "attn_fwd_kernel<128, false>"
+ATTN_KERNEL = "attn_fwd_kernel<128, false, 8>"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_bf16_longvideo_traffic.json")
 
 
