@@ -97,6 +97,9 @@ __device__ __forceinline__ int vswz(int row, int ch) {
   }
 }
 
+// An empty asm that the compiler must assume redefines x (a VGPR value).
+__device__ __forceinline__ void opaque(uint32_t& x) { asm volatile("" : "+v"(x)); }
+
 template <int D, bool INT8, int NW>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2)))
 void attn_fwd_kernel(const uint8_t* __restrict__ qp, const uint8_t* __restrict__ kp,
@@ -176,15 +179,16 @@ void attn_fwd_kernel(const uint8_t* __restrict__ qp, const uint8_t* __restrict__
   }
   // first row of tile kt (uniform); S >= kBK whenever more than one tile exists
   auto tile_row = [&](int kt) { return min(kt * kBK, S - kBK); };
-  // The empty asm keeps each offset a 32-bit value at the load, so the address is selected as
-  // scalar base + 32-bit vector offset (the global "saddr" form) instead of a 64-bit VALU add.
+  // The offsets are redefined (by an empty asm) at the top of every loop iteration, so their
+  // zero extension cannot be hoisted out of the loop and each address is selected as scalar
+  // base + 32-bit vector offset (the global "saddr" form), not a 64-bit VALU add.
   auto load_k = [&](int kt, uint8_t* dst) {
     const uint8_t* tb = kh + (size_t)tile_row(kt) * T::KROW;
     if (T::KPART && wave_u * 64 >= T::KBYTES / 16) return;  // this wave has no K slot
 #pragma unroll
     for (int r = 0; r < T::KLD; ++r) {
-      uint32_t off = kofl[r];
-      asm volatile("" : "+v"(off));
+      const uint32_t off = kofl[r];  // (a subscript inside the builtin's argument drops the
+                                     // kernel's host launch stub with this compiler)
       __builtin_amdgcn_global_load_lds(tb + off, (lds_void*)(dst + (r * kThreads + wave_u * 64) * 16), 16, 0, 0);
     }
   };
@@ -192,8 +196,7 @@ void attn_fwd_kernel(const uint8_t* __restrict__ qp, const uint8_t* __restrict__
     const uint8_t* tb = vh + (size_t)tile_row(kt) * T::VROW;
 #pragma unroll
     for (int r = 0; r < T::VLD; ++r) {
-      uint32_t off = vofl[r];
-      asm volatile("" : "+v"(off));
+      const uint32_t off = vofl[r];
       __builtin_amdgcn_global_load_lds(tb + off, (lds_void*)(dst + (r * kThreads + wave_u * 64) * 16), 16, 0, 0);
     }
   };
@@ -310,11 +313,20 @@ void attn_fwd_kernel(const uint8_t* __restrict__ qp, const uint8_t* __restrict__
     }
     float cf = cq;
     if constexpr (INT8) cf = cq * k_scale[(size_t)bh * nkt + j];
-    float mx = s[0];
+    float mx;
+    if constexpr (INT8) {
+      // biased int8 scores are positive floats (or -inf when masked): their bit patterns order
+      // like signed integers, and the integer maximum needs no NaN canonicalization
+      int mi = __float_as_int(s[0]);
 #pragma unroll
-    for (int r = 1; r < 32; ++r) mx = fmaxf(mx, s[r]);
-    mx = xor32_max(mx);
-    if constexpr (INT8) mx -= kBiasF;  // exact: both are integers below 2^24
+      for (int r = 1; r < 32; ++r) mi = max(mi, __float_as_int(s[r]));
+      mx = __int_as_float(xor32_max_i32(mi)) - kBiasF;  // exact: integers below 2^24
+    } else {
+      mx = s[0];
+#pragma unroll
+      for (int r = 1; r < 32; ++r) mx = fmaxf(mx, s[r]);
+      mx = xor32_max(mx);
+    }
     mx *= cf;
     if (__builtin_amdgcn_ballot_w64(mx > m_run + kLazy) != 0) {
       const float m_new = fmaxf(m_run, mx);
@@ -379,6 +391,10 @@ void attn_fwd_kernel(const uint8_t* __restrict__ qp, const uint8_t* __restrict__
 
   int j = 0;
   for (; j + 1 < nkt; j += 2) {
+#pragma unroll
+    for (int r = 0; r < T::KLD; ++r) opaque(kofl[r]);
+#pragma unroll
+    for (int r = 0; r < T::VLD; ++r) opaque(vofl[r]);
     stage(j, std::integral_constant<int, 0>{}, sa, sb);
     stage(j + 1, std::integral_constant<int, 1>{}, sb, sa);
   }
