@@ -101,9 +101,8 @@ int attn_fwd_int8qk(const void* q, const void* k, const void* v, float* o, int B
   double* partial = reinterpret_cast<double*>(ws + off[5]);
   hipStream_t s = static_cast<hipStream_t>(stream);
 
-  hipError_t e = ditattn::launch_kmean(k, k_mean, partial, B, H, S, D, s);
-  if (e != hipSuccess) return DITATTN_EHIP;
-  e = ditattn::launch_quant_qk(q, k, k_mean, q_codes, k_codes, q_scale, k_scale, B, H, S, D, s);
+  const hipError_t e = ditattn::launch_prepass(q, k, k_mean, partial, q_codes, k_codes, q_scale,
+                                               k_scale, B, H, S, D, s);
   if (e != hipSuccess) return DITATTN_EHIP;
   return status_of(ditattn::launch_attn_int8(q_codes, k_codes, v, o, q_scale, k_scale, B, H, S,
                                              D, scale, s));

@@ -19,15 +19,13 @@ hipError_t launch_attn_int8(const void* q_codes, const void* k_codes, const void
 // Number of token chunks the K-mean partial pass splits each (b, h) into.
 int kmean_chunks(int B, int H, int S);
 
-// K channel mean (exact double-double sum, one division, one rounding to fp32).
-// partial: scratch of B*H*kmean_chunks(B,H,S)*D double pairs.
-hipError_t launch_kmean(const void* k, float* k_mean, double* partial, int B, int H, int S, int D,
-                        hipStream_t stream);
-
-// Per-block int8 quantization of Q (128-token blocks) and smoothed K (64-token blocks).
-hipError_t launch_quant_qk(const void* q, const void* k, const float* k_mean, int8_t* q_codes,
-                           int8_t* k_codes, float* q_scale, float* k_scale, int B, int H, int S,
-                           int D, hipStream_t stream);
+// The int8 prepass: K channel mean (exact double-double sum, one division, one rounding to
+// fp32) and per-block int8 quantization of Q (128-token blocks) and of the mean-smoothed K
+// (64-token blocks).  Three launches: mean partial sums together with the Q blocks, the mean,
+// then the K blocks.  partial: scratch of B*H*kmean_chunks(B,H,S)*D double pairs.
+hipError_t launch_prepass(const void* q, const void* k, float* k_mean, double* partial,
+                          int8_t* q_codes, int8_t* k_codes, float* q_scale, float* k_scale, int B,
+                          int H, int S, int D, hipStream_t stream);
 
 // Number of partial-sum workgroups the relative-L1 pass uses for n elements.
 int rel_l1_blocks(int64_t n);

@@ -13,6 +13,8 @@
 // Q blocks are 128 tokens and K blocks 64 tokens of one (b, h); a tail block covers only the
 // valid tokens.  These kernels are bound by HBM bandwidth: every byte is read once (K twice:
 // once for the mean, once for the codes) and every code written once, with 16-byte accesses.
+// Three launches: the mean's partial sums together with the Q blocks (which do not need the
+// mean), the mean itself, then the K blocks.
 #include "device_common.h"
 #include "kernels.h"
 
@@ -24,16 +26,16 @@ constexpr int kThreads = 256;
 
 // ---- K channel mean: exact double-double partial sums over token chunks ------------------
 template <int D>
-__global__ __launch_bounds__(kThreads) void kmean_partial_kernel(const uint16_t* __restrict__ k,
-                                                                 double* __restrict__ partial,
-                                                                 int S, int nch, int rows_per) {
+__device__ __forceinline__ void kmean_partial(const uint16_t* __restrict__ k,
+                                              double* __restrict__ partial, int S, int nch,
+                                              int rows_per, int id) {
   constexpr int TPR = D / 8;             // threads per token row (8 channels each)
   constexpr int RPP = kThreads / TPR;    // rows per pass
   __shared__ double red_hi[kThreads][8];
   __shared__ double red_lo[kThreads][8];
 
-  const int bh = blockIdx.x / nch;
-  const int chunk = blockIdx.x - bh * nch;
+  const int bh = id / nch;
+  const int chunk = id - bh * nch;
   const int tid = threadIdx.x;
   const int cg = tid % TPR, rg = tid / TPR;
   const int r0 = chunk * rows_per;
@@ -41,14 +43,25 @@ __global__ __launch_bounds__(kThreads) void kmean_partial_kernel(const uint16_t*
   const uint16_t* kh = k + (size_t)bh * S * D;
 
   DDSum acc[8];
-  for (int row = r0 + rg; row < r1; row += RPP) {
-    const u32x4 x = *reinterpret_cast<const u32x4*>(kh + (size_t)row * D + cg * 8);
+  auto add_row = [&](const u32x4& x) {
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
       acc[2 * w].add((double)bf16lo(x[w]));
       acc[2 * w + 1].add((double)bf16hi(x[w]));
     }
+  };
+  // eight rows' loads in flight before their (long, dependent) double-double additions
+  constexpr int U = 8;
+  int row = r0 + rg;
+  for (; row + (U - 1) * RPP < r1; row += U * RPP) {
+    u32x4 x[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      x[u] = *reinterpret_cast<const u32x4*>(kh + (size_t)(row + u * RPP) * D + cg * 8);
+#pragma unroll
+    for (int u = 0; u < U; ++u) add_row(x[u]);
   }
+  for (; row < r1; row += RPP) add_row(*reinterpret_cast<const u32x4*>(kh + (size_t)row * D + cg * 8));
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
     red_hi[tid][e] = acc[e].hi;
@@ -147,6 +160,12 @@ __device__ __forceinline__ void quant_block(const uint16_t* __restrict__ x, cons
   amax = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
   const float scale = (amax == 0.f) ? 1.0f : amax / 127.0f;
   if (tid == 0) *scale_out = scale;
+  // fl32(x / scale) is computed as fl32(fl64(x * fl64(1 / scale))), which is the same value
+  // for every fp32 x and scale: the fp64 product is within 2^-52 (relative) of x / scale, while
+  // a quotient of two 24-bit significands is either an fp32 rounding midpoint exactly (which
+  // needs 25 significant bits, so never) or at least 2^-49 away from every midpoint.  Zero,
+  // infinite and NaN operands give the same special values both ways.
+  const double rinv = 1.0 / (double)scale;
 
 #pragma unroll
   for (int r = 0; r < NC; ++r) {
@@ -156,7 +175,7 @@ __device__ __forceinline__ void quant_block(const uint16_t* __restrict__ x, cons
     uint32_t packed[2] = {0u, 0u};
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      float qv = rintf(v[r][e] / scale);
+      float qv = rintf((float)((double)v[r][e] * rinv));
       qv = fminf(fmaxf(qv, -127.f), 127.f);
       packed[e >> 2] |= ((uint32_t)(uint8_t)(int8_t)(int)qv) << (8 * (e & 3));
     }
@@ -164,24 +183,32 @@ __device__ __forceinline__ void quant_block(const uint16_t* __restrict__ x, cons
   }
 }
 
+// First pass of the prepass: the K-mean partial sums (ids below BH * nch) and, independent of
+// the mean, the Q blocks (the remaining ids) in one launch.
 template <int D>
-__global__ __launch_bounds__(kThreads) void quant_qk_kernel(const uint16_t* __restrict__ q,
-                                                            const uint16_t* __restrict__ k,
-                                                            const float* __restrict__ k_mean,
-                                                            int8_t* __restrict__ q_codes,
-                                                            int8_t* __restrict__ k_codes,
-                                                            float* __restrict__ q_scale,
-                                                            float* __restrict__ k_scale, int S,
-                                                            int BH, int nqb, int nkb) {
+__global__ __launch_bounds__(kThreads) void kmean_partial_quant_q_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, double* __restrict__ partial,
+    int8_t* __restrict__ q_codes, float* __restrict__ q_scale, int S, int BH, int nch, int rows_per,
+    int nqb) {
   const int id = blockIdx.x;
-  if (id < BH * nqb) {
-    const int bh = id / nqb, blk = id - bh * nqb;
-    quant_block<D, 128, false>(q, nullptr, q_codes, q_scale + (size_t)bh * nqb + blk, S, bh, blk);
+  if (id < BH * nch) {
+    kmean_partial<D>(k, partial, S, nch, rows_per, id);
   } else {
-    const int j = id - BH * nqb;
-    const int bh = j / nkb, blk = j - bh * nkb;
-    quant_block<D, 64, true>(k, k_mean, k_codes, k_scale + (size_t)bh * nkb + blk, S, bh, blk);
+    const int j = id - BH * nch;
+    const int bh = j / nqb, blk = j - bh * nqb;
+    quant_block<D, 128, false>(q, nullptr, q_codes, q_scale + (size_t)bh * nqb + blk, S, bh, blk);
   }
+}
+
+// Last pass: the K blocks, smoothed by the finished mean.
+template <int D>
+__global__ __launch_bounds__(kThreads) void quant_k_kernel(const uint16_t* __restrict__ k,
+                                                           const float* __restrict__ k_mean,
+                                                           int8_t* __restrict__ k_codes,
+                                                           float* __restrict__ k_scale, int S,
+                                                           int nkb) {
+  const int bh = blockIdx.x / nkb, blk = blockIdx.x - bh * nkb;
+  quant_block<D, 64, true>(k, k_mean, k_codes, k_scale + (size_t)bh * nkb + blk, S, bh, blk);
 }
 
 }  // namespace
@@ -194,38 +221,31 @@ int kmean_chunks(int B, int H, int S) {
   return (int)(n < 1 ? 1 : n);
 }
 
-hipError_t launch_kmean(const void* k, float* k_mean, double* partial, int B, int H, int S, int D,
-                        hipStream_t stream) {
+template <int D>
+hipError_t launch_prepass_d(const uint16_t* q, const uint16_t* k, float* k_mean, double* partial,
+                            int8_t* q_codes, int8_t* k_codes, float* q_scale, float* k_scale,
+                            int B, int H, int S, hipStream_t stream) {
+  const int BH = B * H;
   const int nch = kmean_chunks(B, H, S);
   const int rows_per = (S + nch - 1) / nch;
-  const unsigned bh = (unsigned)(B * H);
-  if (D == 64) {
-    hipLaunchKernelGGL(kmean_partial_kernel<64>, dim3(bh * nch), dim3(kThreads), 0, stream,
-                       static_cast<const uint16_t*>(k), partial, S, nch, rows_per);
-    hipLaunchKernelGGL(kmean_final_kernel<64>, dim3(bh), dim3(kThreads), 0, stream, partial, k_mean, S, nch);
-  } else {
-    hipLaunchKernelGGL(kmean_partial_kernel<128>, dim3(bh * nch), dim3(kThreads), 0, stream,
-                       static_cast<const uint16_t*>(k), partial, S, nch, rows_per);
-    hipLaunchKernelGGL(kmean_final_kernel<128>, dim3(bh), dim3(kThreads), 0, stream, partial, k_mean, S, nch);
-  }
+  const int nqb = (S + 127) / 128, nkb = (S + 63) / 64;
+  hipLaunchKernelGGL(kmean_partial_quant_q_kernel<D>, dim3((unsigned)((long long)BH * (nch + nqb))),
+                     dim3(kThreads), 0, stream, q, k, partial, q_codes, q_scale, S, BH, nch, rows_per, nqb);
+  hipLaunchKernelGGL(kmean_final_kernel<D>, dim3((unsigned)BH), dim3(kThreads), 0, stream, partial,
+                     k_mean, S, nch);
+  hipLaunchKernelGGL(quant_k_kernel<D>, dim3((unsigned)((long long)BH * nkb)), dim3(kThreads), 0,
+                     stream, k, k_mean, k_codes, k_scale, S, nkb);
   return hipGetLastError();
 }
 
-hipError_t launch_quant_qk(const void* q, const void* k, const float* k_mean, int8_t* q_codes,
-                           int8_t* k_codes, float* q_scale, float* k_scale, int B, int H, int S,
-                           int D, hipStream_t stream) {
-  const int BH = B * H;
-  const int nqb = (S + 127) / 128, nkb = (S + 63) / 64;
-  const dim3 grid((unsigned)((long long)BH * (nqb + nkb)));
+hipError_t launch_prepass(const void* q, const void* k, float* k_mean, double* partial,
+                          int8_t* q_codes, int8_t* k_codes, float* q_scale, float* k_scale, int B,
+                          int H, int S, int D, hipStream_t stream) {
+  const auto* qq = static_cast<const uint16_t*>(q);
+  const auto* kk = static_cast<const uint16_t*>(k);
   if (D == 64)
-    hipLaunchKernelGGL(quant_qk_kernel<64>, grid, dim3(kThreads), 0, stream,
-                       static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k), k_mean,
-                       q_codes, k_codes, q_scale, k_scale, S, BH, nqb, nkb);
-  else
-    hipLaunchKernelGGL(quant_qk_kernel<128>, grid, dim3(kThreads), 0, stream,
-                       static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k), k_mean,
-                       q_codes, k_codes, q_scale, k_scale, S, BH, nqb, nkb);
-  return hipGetLastError();
+    return launch_prepass_d<64>(qq, kk, k_mean, partial, q_codes, k_codes, q_scale, k_scale, B, H, S, stream);
+  return launch_prepass_d<128>(qq, kk, k_mean, partial, q_codes, k_codes, q_scale, k_scale, B, H, S, stream);
 }
 
 }  // namespace ditattn
