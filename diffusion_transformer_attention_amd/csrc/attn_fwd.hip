@@ -28,9 +28,12 @@
 //   * int8 scores leave the matrix cores already as fp32: the integer accumulator starts at
 //     the bit pattern of 1.5 * 2^23, so its final bits read as fp32 are 1.5 * 2^23 plus the
 //     score, exactly; the bias folds into the exponent offset (no conversion instructions).
-//   * Lazy rescale: m only moves when a tile's maximum exceeds it by more than 8 (log2
-//     domain); otherwise weights up to 2^8 are used as they are (bf16 and fp32 hold them with
-//     full relative precision).  On typical data O is rescaled a handful of times per row.
+//   * Lazy, optimistic rescale: the weights of a tile are formed with the current offset m
+//     straight away; only when one would exceed 2^8 (seen through each lane's sum of its
+//     weights, which bounds them all) does the tile take its row maximum, move m, rescale O
+//     and redo the weights.  Weights up to 2^8 are used as they are (bf16 and fp32 hold them
+//     with full relative precision); on typical data m moves a handful of times per row, so
+//     the row maximum is almost never computed.
 //   * Workgroup ids are remapped so the workgroups the dispatcher places on one XCD (ids
 //     congruent mod 8) process consecutive query tiles of the same head and share its K/V
 //     stream in that XCD's L2.
@@ -46,7 +49,7 @@ namespace {
 constexpr int kQBlock = 128;    // int8 Q quantization block (tokens)
 constexpr int kBK = 64;         // keys per tile (= int8 K block)
 constexpr float kLog2e = 1.4426950408889634f;
-constexpr float kLazy = 8.0f;   // log2-domain headroom before the running max moves
+constexpr float kLazyW = 256.0f;  // 2^8: largest weight (and lane weight sum) kept as it is
 // 1.5 * 2^23: every fp32 in [2^23, 2^24) is an integer and consecutive integers have
 // consecutive bit patterns, so bits(kBiasF) + n read as fp32 is kBiasF + n for |n| < 2^22.
 // An int8 score is at most 127 * 127 * 128 < 2^21 in magnitude, so the int8 QK product
@@ -313,48 +316,59 @@ void attn_fwd_kernel(const uint8_t* __restrict__ qp, const uint8_t* __restrict__
     }
     float cf = cq;
     if constexpr (INT8) cf = cq * k_scale[(size_t)bh * nkt + j];
-    float mx;
-    if constexpr (INT8) {
-      // biased int8 scores are positive floats (or -inf when masked): their bit patterns order
-      // like signed integers, and the integer maximum needs no NaN canonicalization
-      int mi = __float_as_int(s[0]);
+    // S[j+1] on the matrix cores (K[j+1] is resident) while the VALU forms P[j]
+    qk(kb_next, sn);
+
+    // P[j] with the current offset m_run, optimistically: the tile's row maximum is only
+    // needed when some weight would exceed kLazyW, and this lane's sum of its 32 bf16 weights
+    // bounds every one of them.  A sum above kLazyW (or inf / NaN, e.g. on the first tile)
+    // sends the wave to the rare path, which takes the maximum, moves m_run, rescales O and l
+    // and recomputes the weights.
+    bf16x8 pb[4];
+    float lt;
+    auto weights = [&]() __attribute__((always_inline)) {
+      // exponent offset: m_run, plus the bias carried by the int8 scores (cf * kBiasF, rounded
+      // once; its error is far below the int8 quantization error of the scores themselves)
+      const float mb = INT8 ? fmaf(cf, kBiasF, m_run) : m_run;
 #pragma unroll
-      for (int r = 1; r < 32; ++r) mi = max(mi, __float_as_int(s[r]));
-      mx = __int_as_float(xor32_max_i32(mi)) - kBiasF;  // exact: integers below 2^24
-    } else {
-      mx = s[0];
+      for (int c4 = 0; c4 < 4; ++c4)
 #pragma unroll
-      for (int r = 1; r < 32; ++r) mx = fmaxf(mx, s[r]);
-      mx = xor32_max(mx);
-    }
-    mx *= cf;
-    if (__builtin_amdgcn_ballot_w64(mx > m_run + kLazy) != 0) {
-      const float m_new = fmaxf(m_run, mx);
+        for (int e = 0; e < 8; ++e)
+          pb[c4][e] = (__bf16)__builtin_amdgcn_exp2f(fmaf(s[8 * c4 + e], cf, -mb));
+      // row sum of the bf16 weights that enter PV, two at a time on the dot unit
+      const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+      lt = 0.f;
+#pragma unroll
+      for (int c4 = 0; c4 < 4; ++c4)
+#pragma unroll
+        for (int e = 0; e < 8; e += 2)
+          lt = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pb[c4][e], pb[c4][e + 1]}, ones, lt, false);
+    };
+    weights();
+    if (__builtin_amdgcn_ballot_w64(!(lt <= kLazyW)) != 0) {
+      float mx;
+      if constexpr (INT8) {
+        // biased int8 scores are positive floats (or -inf when masked): their bit patterns
+        // order like signed integers
+        int mi = __float_as_int(s[0]);
+#pragma unroll
+        for (int r = 1; r < 32; ++r) mi = max(mi, __float_as_int(s[r]));
+        mx = __int_as_float(xor32_max_i32(mi)) - kBiasF;  // exact: integers below 2^24
+      } else {
+        mx = s[0];
+#pragma unroll
+        for (int r = 1; r < 32; ++r) mx = fmaxf(mx, s[r]);
+        mx = xor32_max(mx);
+      }
+      const float m_new = fmaxf(m_run, mx * cf);
       const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
       m_run = m_new;
       l_run *= alpha;
 #pragma unroll
       for (int db = 0; db < T::NDB; ++db) oacc[db] *= alpha;
+      weights();
     }
-
-    // exponent offset: m_run, plus the bias carried by the int8 scores (cf * kBiasF, rounded
-    // once; its error is far below the int8 quantization error of the scores themselves)
-    const float mb = INT8 ? fmaf(cf, kBiasF, m_run) : m_run;
-    // S[j+1] on the matrix cores (K[j+1] is resident) while the VALU forms P[j]
-    qk(kb_next, sn);
-    bf16x8 pb[4];
-#pragma unroll
-    for (int c4 = 0; c4 < 4; ++c4)
-#pragma unroll
-      for (int e = 0; e < 8; ++e)
-        pb[c4][e] = (__bf16)__builtin_amdgcn_exp2f(fmaf(s[8 * c4 + e], cf, -mb));
-    // row sum of the bf16 weights that enter PV, two at a time on the dot unit
-    const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
-#pragma unroll
-    for (int c4 = 0; c4 < 4; ++c4)
-#pragma unroll
-      for (int e = 0; e < 8; e += 2)
-        l_run = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pb[c4][e], pb[c4][e + 1]}, ones, l_run, false);
+    l_run += lt;
 
     // O^T += V[j]^T P[j]: lane holds channels 32 db + 8 (r / 4) + 4 hh + r % 4, query q
 #pragma unroll
