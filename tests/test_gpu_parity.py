@@ -134,6 +134,38 @@ def test_bf16_deterministic():
     assert torch.equal(a, b)
 
 
+def _rising_scores_inputs(S=1000, D=128, H=2, seed=600):
+    """Scores that climb along the key axis (~+20 in log2 units per 64-key tile, so the running
+    maximum moves on every tile), plus one early key (tile 2) about 250 above everything seen
+    so far: weights formed with the stale offset overflow to inf there.  The ramp later
+    catches up with that key, so the result is not a one-hot average."""
+    rng = np.random.default_rng(seed)
+    w = np.full(D, 4.0 / np.sqrt(D))
+    q = 0.5 * rng.standard_normal((1, H, S, D)) + w
+    lam = np.linspace(0.0, 180.0, S)
+    lam[150] = 174.0
+    k = rng.standard_normal((1, H, S, D)) + lam[None, None, :, None] * w
+    v = rng.standard_normal((1, H, S, D))
+    return tuple(datagen.f64_to_bf16_bits(x) for x in (q, k, v))
+
+
+def test_bf16_running_max_moves_every_tile():
+    announce("attn_fwd_bf16 rising scores B1 H2 S1000 D128")
+    q, k, v = _rising_scores_inputs()
+    got = run_bf16(q, k, v).cpu().numpy()
+    check_bf16(got, oracle.attention(f64(q), f64(k), f64(v)), "rising scores")
+
+
+def test_int8_running_max_moves_every_tile():
+    announce("attn_fwd_int8qk rising scores B1 H2 S1000 D128")
+    q, k, v = _rising_scores_inputs()
+    out, views = run_int8(q, k, v)
+    ref = oracle.quantize_qk(f64(q), f64(k))
+    check_quant_exact(views, ref, "rising scores")
+    oq = oracle.attention_int8(ref["q_codes"], ref["q_scale"], ref["k_codes"], ref["k_scale"], f64(v))
+    check_int8_out(out.cpu().numpy(), oq, oracle.attention(f64(q), f64(k), f64(v)), "rising scores")
+
+
 @pytest.fixture(scope="module")
 def image_inputs():
     return datagen.attention_inputs("image")
