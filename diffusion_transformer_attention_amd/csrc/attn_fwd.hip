@@ -291,22 +291,13 @@ void attn_fwd_kernel(const uint8_t* __restrict__ qp, const uint8_t* __restrict__
     }
   };
 
-  // One pipeline stage: softmax of tile j (scores in `s`), S[j+1] into `sn`, O += V[j]^T P[j].
-  auto stage = [&](int j, auto par_c, float (&s)[32], float (&sn)[32]) {
-    constexpr int par = decltype(par_c)::value;
-    uint8_t* const kb_cur = par ? kbuf_1 : kbuf_0;    // held K[j]; receives K[j+2]
-    uint8_t* const kb_next = par ? kbuf_0 : kbuf_1;   // holds K[j+1]
-    uint8_t* const vb_cur = par ? vbuf_1 : vbuf_0;    // holds V[j]
-    uint8_t* const vb_next = par ? vbuf_0 : vbuf_1;   // receives V[j+1]
-    if (j + 2 < nkt) load_k(j + 2, kb_cur);
-    if (j + 1 < nkt) load_v(j + 1, vb_next);
-
-    if (j == nkt - 1 && (S % kBK) != 0) {
-      // keys of this tile outside [j * kBK, S): already seen in tile j - 1, or past the end.
-      // In tile-local key numbers the valid range is [lo, hi); the empty asm keeps the
-      // comparisons inside this rarely taken branch.
-      const int t0 = tile_row(j) > 0 ? tile_row(j) : 0;
-      int lo = j * kBK - t0 - 4 * hh, hi = S - t0 - 4 * hh;
+  // Masks the keys tile jt does not own (a partial last tile: keys outside [jt * kBK, S) were
+  // already seen in tile jt - 1, or lie past the end).  In tile-local key numbers the valid
+  // range is [lo, hi); the empty asm keeps the comparisons inside the rarely taken branch.
+  auto mask_tile = [&](int jt, float (&s)[32]) __attribute__((always_inline)) {
+    if (jt == nkt - 1 && (S % kBK) != 0) {
+      const int t0 = tile_row(jt) > 0 ? tile_row(jt) : 0;
+      int lo = jt * kBK - t0 - 4 * hh, hi = S - t0 - 4 * hh;
       asm volatile("" : "+v"(lo), "+v"(hi));
 #pragma unroll
       for (int r = 0; r < 32; ++r) {
@@ -314,38 +305,42 @@ void attn_fwd_kernel(const uint8_t* __restrict__ qp, const uint8_t* __restrict__
         if (kc < lo || kc >= hi) s[r] = -INFINITY;
       }
     }
-    float cf = cq;
-    if constexpr (INT8) cf = cq * k_scale[(size_t)bh * nkt + j];
-    // S[j+1] on the matrix cores (K[j+1] is resident) while the VALU forms P[j]
-    qk(kb_next, sn);
+  };
 
-    // P[j] with the current offset m_run, optimistically: the tile's row maximum is only
-    // needed when some weight would exceed kLazyW, and this lane's sum of its 32 bf16 weights
-    // bounds every one of them.  A sum above kLazyW (or inf / NaN, e.g. on the first tile)
-    // sends the wave to the rare path, which takes the maximum, moves m_run, rescales O and l
-    // and recomputes the weights.
-    bf16x8 pb[4];
-    float lt;
-    auto weights = [&]() __attribute__((always_inline)) {
-      // exponent offset: m_run, plus the bias carried by the int8 scores (cf * kBiasF, rounded
-      // once; its error is far below the int8 quantization error of the scores themselves)
-      const float mb = INT8 ? fmaf(cf, kBiasF, m_run) : m_run;
+  // P of tile jt from its scores, optimistically with the current offset m_run: the tile's
+  // row maximum is only needed when some weight would exceed kLazyW, and this lane's sum of
+  // its 32 bf16 weights (lt) bounds every one of them.
+  auto weights = [&](int jt, const float (&s)[32], bf16x8 (&pb)[4], float& lt, float& cf)
+                     __attribute__((always_inline)) {
+    cf = cq;
+    if constexpr (INT8) cf = cq * k_scale[(size_t)bh * nkt + min(jt, nkt - 1)];
+    // exponent offset: m_run, plus the bias carried by the int8 scores (cf * kBiasF, rounded
+    // once; its error is far below the int8 quantization error of the scores themselves)
+    const float mb = INT8 ? fmaf(cf, kBiasF, m_run) : m_run;
 #pragma unroll
-      for (int c4 = 0; c4 < 4; ++c4)
+    for (int c4 = 0; c4 < 4; ++c4)
 #pragma unroll
-        for (int e = 0; e < 8; ++e)
-          pb[c4][e] = (__bf16)__builtin_amdgcn_exp2f(fmaf(s[8 * c4 + e], cf, -mb));
-      // row sum of the bf16 weights that enter PV, two at a time on the dot unit
-      const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
-      lt = 0.f;
+      for (int e = 0; e < 8; ++e)
+        pb[c4][e] = (__bf16)__builtin_amdgcn_exp2f(fmaf(s[8 * c4 + e], cf, -mb));
+    // row sum of the bf16 weights that enter PV, two at a time on the dot unit
+    const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+    lt = 0.f;
 #pragma unroll
-      for (int c4 = 0; c4 < 4; ++c4)
+    for (int c4 = 0; c4 < 4; ++c4)
 #pragma unroll
-        for (int e = 0; e < 8; e += 2)
-          lt = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pb[c4][e], pb[c4][e + 1]}, ones, lt, false);
-    };
-    weights();
+      for (int e = 0; e < 8; e += 2)
+        lt = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pb[c4][e], pb[c4][e + 1]}, ones, lt, false);
+  };
+
+  // The rare path: a lane's weight sum above kLazyW (or inf / NaN, e.g. on the first tile)
+  // makes the wave take the tile's row maximum, move m_run, rescale O and l (which then hold
+  // the tiles before jt) and recompute the weights of tile jt.
+  auto settle = [&](int jt, const float (&s)[32], bf16x8 (&pb)[4], float& lt)
+                    __attribute__((always_inline)) {
+    float cf;
     if (__builtin_amdgcn_ballot_w64(!(lt <= kLazyW)) != 0) {
+      cf = cq;
+      if constexpr (INT8) cf = cq * k_scale[(size_t)bh * nkt + jt];
       float mx;
       if constexpr (INT8) {
         // biased int8 scores are positive floats (or -inf when masked): their bit patterns
@@ -366,9 +361,28 @@ void attn_fwd_kernel(const uint8_t* __restrict__ qp, const uint8_t* __restrict__
       l_run *= alpha;
 #pragma unroll
       for (int db = 0; db < T::NDB; ++db) oacc[db] *= alpha;
-      weights();
+      weights(jt, s, pb, lt, cf);
     }
     l_run += lt;
+  };
+
+  // One pipeline stage j: S[j+2] = K[j+2] Q^T on the matrix cores, the weights P[j+1] of
+  // S[j+1] on the VALU, and O += V[j]^T P[j] — three independent streams in one basic block —
+  // then the rare rescale for tile j + 1, which must follow the PV products of tile j.
+  auto stage = [&](int j, auto par_c, float (&s1)[32], float (&s2)[32], bf16x8 (&p0)[4],
+                   bf16x8 (&p1)[4]) __attribute__((always_inline)) {
+    constexpr int par = decltype(par_c)::value;
+    uint8_t* const kb_read = par ? kbuf_1 : kbuf_0;   // holds K[j+2]
+    uint8_t* const kb_fill = par ? kbuf_0 : kbuf_1;   // held K[j+1]; receives K[j+3]
+    uint8_t* const vb_cur = par ? vbuf_1 : vbuf_0;    // holds V[j]
+    uint8_t* const vb_next = par ? vbuf_0 : vbuf_1;   // receives V[j+1]
+    if (j + 3 < nkt) load_k(j + 3, kb_fill);
+    if (j + 1 < nkt) load_v(j + 1, vb_next);
+
+    // (past the last tile these compute on stale data and are discarded)
+    qk(kb_read, s2);
+    float lt, cf;
+    weights(j + 1, s1, p1, lt, cf);
 
     // O^T += V[j]^T P[j]: lane holds channels 32 db + 8 (r / 4) + 4 hh + r % 4, query q
 #pragma unroll
@@ -380,16 +394,18 @@ void attn_fwd_kernel(const uint8_t* __restrict__ qp, const uint8_t* __restrict__
         const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(base + 8 * T::VROW));
         const u32x2 lo2 = __builtin_bit_cast(u32x2, lo), hi2 = __builtin_bit_cast(u32x2, hi);
         const u32x4 a = {lo2[0], lo2[1], hi2[0], hi2[1]};
-        oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), pb[c4],
+        oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), p0[c4],
                                                            oacc[db], 0, 0, 0);
       }
     }
-    // the loads into kb_cur / vb_next must land before any wave reads them
+    if (j + 1 < nkt) settle(j + 1, s1, p1, lt);
+    mask_tile(j + 2, s2);
+    // the loads into kb_fill / vb_next must land before any wave reads them
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
     __syncthreads();
   };
 
-  // ---- prologue: K[0], K[1], V[0] resident; S[0] computed ---------------------------------
+  // ---- prologue: S[0], S[1] and P[0] computed; K[2] and V[0] resident ---------------------
   if (S < kBK) {
     load_short(kbuf_0, vbuf_0);
   } else {
@@ -400,19 +416,32 @@ void attn_fwd_kernel(const uint8_t* __restrict__ qp, const uint8_t* __restrict__
   __builtin_amdgcn_s_waitcnt(0x0F70);
   __syncthreads();
   float sa[32], sb[32];
+  bf16x8 pa[4], pbb[4];
   qk(kbuf_0, sa);
-  __syncthreads();  // every wave has read K[0] before its buffer receives K[2]
+  if (nkt > 1) qk(kbuf_1, sb);
+  __syncthreads();  // every wave has read K[0] and K[1]
+  if (nkt > 2) load_k(2, kbuf_0);
+  mask_tile(0, sa);
+  if (nkt > 1) mask_tile(1, sb);
+  {
+    float lt, cf;
+    weights(0, sa, pa, lt, cf);
+    settle(0, sa, pa, lt);
+  }
+  __builtin_amdgcn_s_waitcnt(0x0F70);
+  __syncthreads();
 
+  // stage j reads S[j+1] and writes S[j+2]; consumes P[j] and produces P[j+1]
   int j = 0;
   for (; j + 1 < nkt; j += 2) {
 #pragma unroll
     for (int r = 0; r < T::KLD; ++r) opaque(kofl[r]);
 #pragma unroll
     for (int r = 0; r < T::VLD; ++r) opaque(vofl[r]);
-    stage(j, std::integral_constant<int, 0>{}, sa, sb);
-    stage(j + 1, std::integral_constant<int, 1>{}, sb, sa);
+    stage(j, std::integral_constant<int, 0>{}, sb, sa, pa, pbb);
+    stage(j + 1, std::integral_constant<int, 1>{}, sa, sb, pbb, pa);
   }
-  if (j < nkt) stage(j, std::integral_constant<int, 0>{}, sa, sb);
+  if (j < nkt) stage(j, std::integral_constant<int, 0>{}, sb, sa, pa, pbb);
 
   // ---- epilogue: O = O_acc / l, fp32 ---------------------------------------------------
   const float inv = 1.f / xor32_sum(l_run);
