@@ -22,9 +22,10 @@
 //     instruction, so the XOR swizzle of 16-byte chunks is applied to the *global* address a
 //     lane fetches: LDS slot p holds the chunk that belongs at p in the swizzled layout.  The
 //     swizzles make every 16- and 32-lane phase of the MFMA operand reads conflict-free.
-//   * Software pipeline: K runs two tiles ahead of V.  Iteration j issues the loads of K[j+2]
-//     and V[j+1], computes S[j+1] = K[j+1] Q^T on the matrix cores while the VALU turns S[j]
-//     into P[j], then accumulates O += V[j]^T P[j]; one barrier per iteration.
+//   * Software pipeline, three independent streams per stage in one basic block: stage j
+//     computes S[j+2] = K[j+2] Q^T on the matrix cores, turns S[j+1] into the weights P[j+1]
+//     on the VALU, and accumulates O += V[j]^T P[j]; it issues the loads of K[j+3] and V[j+1]
+//     (K runs three tiles ahead of V); one barrier per stage.
 //   * int8 scores leave the matrix cores already as fp32: the integer accumulator starts at
 //     the bit pattern of 1.5 * 2^23, so its final bits read as fp32 are 1.5 * 2^23 plus the
 //     score, exactly; the bias folds into the exponent offset (no conversion instructions).
@@ -160,12 +161,13 @@ void attn_fwd_kernel(const uint8_t* __restrict__ qp, const uint8_t* __restrict__
   // ---- direct global -> LDS tile loads ------------------------------------------------
   // Slot p (16 bytes) of a tile is written by lane p % 64 of wave (p / 64) % NW in
   // instruction p / (64 NW) (an int8 D = 64 K tile has fewer slots than threads: the waves
-  // past its end skip it).  The byte offset each lane fetches from, relative to the tile's first row, is
-  // loop invariant (one VGPR per instruction) and the tile base is wave-uniform, so a load is
-  // one global_load_lds with a scalar base and no vector address arithmetic.  Every tile is
-  // a full 64 rows: a partial last tile is read as the last 64 rows of the sequence instead
-  // (keys it shares with the previous tile are masked to -inf, so they get weight 0), and only
-  // a sequence shorter than one tile clamps its rows to the last one.
+  // past its end skip it).  The byte offset each lane fetches from, relative to the tile's
+  // first row, is loop invariant (one VGPR per instruction) and the tile base is
+  // wave-uniform, so a load is one global_load_lds with a scalar base and no vector address
+  // arithmetic.  Every tile is a full 64 rows: a partial last tile is read as the last 64
+  // rows of the sequence instead (keys it shares with the previous tile are masked to -inf,
+  // so they get weight 0), and only a sequence shorter than one tile clamps its rows to the
+  // last one.
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);
   uint32_t kofl[T::KLD], vofl[T::VLD];
 #pragma unroll
@@ -242,7 +244,7 @@ void attn_fwd_kernel(const uint8_t* __restrict__ qp, const uint8_t* __restrict__
   f32x16 oacc[T::NDB];
 #pragma unroll
   for (int db = 0; db < T::NDB; ++db) oacc[db] = f32x16{};
-  float m_run = -INFINITY;  // running max of the scaled (log2-domain) scores of row q
+  float m_run = -INFINITY;  // offset of row q's weights: a past maximum of its scaled scores
   float l_run = 0.f;        // this lane's share of the running row sum
 
   i32x16 ibias;
