@@ -6,15 +6,15 @@ baseline leg may import or run it; the library and its Python binding never do, 
 package imports nothing from them (the two share no code; inputs come from ``datagen``).
 
 Modules:
-  attention  -- exact softmax attention (fp64)
+  attention  -- exact softmax attention and its per-row log-sum-exp (fp64)
   quant      -- K channel mean, per-block symmetric int8 quantization, quantized attention
   rel_l1     -- relative L1 distance of two residual tensors
 """
-from .attention import attention, attention_rows
+from .attention import attention, attention_rows, log_sum_exp
 from .quant import (k_channel_mean, smooth_k, quantize_blocks, quantize_qk,
-                    attention_int8, dequantize_blocks, Q_BLOCK, K_BLOCK, QMAX)
+                    attention_int8, dequantize_blocks, log_sum_exp_int8, Q_BLOCK, K_BLOCK, QMAX)
 from .rel_l1 import rel_l1
 
-__all__ = ["attention", "attention_rows", "k_channel_mean", "smooth_k", "quantize_blocks",
+__all__ = ["attention", "attention_rows", "log_sum_exp", "log_sum_exp_int8", "k_channel_mean", "smooth_k", "quantize_blocks",
            "quantize_qk", "attention_int8", "dequantize_blocks", "rel_l1", "Q_BLOCK", "K_BLOCK",
            "QMAX"]

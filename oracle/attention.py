@@ -16,6 +16,14 @@ default of scaled_dot_product_attention, 1/sqrt(D), is what callers pass.
 Subtracting the row maximum before exp changes nothing mathematically (the factor cancels in
 the ratio) and keeps exp from overflowing.  Output rows are independent, so the loop over
 query-row chunks below only bounds memory; it does not reorder any row's arithmetic.
+
+The log-sum-exp of a row, lse_i = log sum_j exp(s_j), is the log of that ratio's denominator.
+It is what lets results over disjoint key sets be merged exactly,
+
+    lse = log(exp(lse_A) + exp(lse_B)),   o = exp(lse_A - lse) o_A + exp(lse_B - lse) o_B,
+
+which is how a sequence split over devices (the ring dimension of the "ParaAttention" page's
+context-parallel mesh, Context Parallelism section) combines its partial attention outputs.
 """
 from __future__ import annotations
 
@@ -59,3 +67,24 @@ def attention_rows(q, k, v, rows, scale: float | None = None) -> np.ndarray:
     """
     q = np.asarray(q, dtype=np.float64)
     return attention(q[:, :, np.asarray(rows)], k, v, scale)
+
+
+def log_sum_exp(q, k, scale: float | None = None) -> np.ndarray:
+    """lse[b, h, i] = log sum_j exp(scale * q_i . k_j) over all keys, fp64 [B, H, Sq].
+
+    q: [B, H, Sq, D]; k: [B, H, Sk, D].  Computed as m + log(sum_j exp(s_j - m)), m = max_j s_j.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    B, H, Sq, D = q.shape
+    if scale is None:
+        scale = 1.0 / np.sqrt(D)
+    out = np.empty((B, H, Sq), dtype=np.float64)
+    for b in range(B):
+        for h in range(H):
+            kt = np.ascontiguousarray(k[b, h].T)
+            for r0 in range(0, Sq, _ROW_CHUNK):
+                sc = (q[b, h, r0:r0 + _ROW_CHUNK] @ kt) * scale
+                m = sc.max(axis=1)
+                out[b, h, r0:r0 + _ROW_CHUNK] = m + np.log(np.exp(sc - m[:, None]).sum(axis=1))
+    return out

@@ -138,3 +138,28 @@ def attention_int8(q_codes, q_scale, k_codes, k_scale, v, scale: float | None = 
                 w = np.exp(s - s.max(axis=1, keepdims=True))
                 out[b, h, r0:r0 + 1024] = (w @ v[b, h]) / w.sum(axis=1, keepdims=True)
     return out
+
+
+def log_sum_exp_int8(q_codes, q_scale, k_codes, k_scale, scale: float | None = None,
+                     q_block: int = Q_BLOCK, k_block: int = K_BLOCK) -> np.ndarray:
+    """log sum_j exp(s_ij) of the int8-path scores (rule 6: s = codes . codes x scales x scale),
+    fp64 [B, H, S] — the normaliser that goes with attention_int8."""
+    q_codes = np.asarray(q_codes)
+    k_codes = np.asarray(k_codes)
+    B, H, S, D = q_codes.shape
+    if scale is None:
+        scale = 1.0 / np.sqrt(D)
+    rows = np.arange(S)
+    sq_rows = np.asarray(q_scale, dtype=np.float64)[:, :, rows // q_block]
+    sk_cols = np.repeat(np.asarray(k_scale, dtype=np.float64), k_block, axis=2)[:, :, :k_codes.shape[2]]
+    out = np.empty((B, H, S), dtype=np.float64)
+    for b in range(B):
+        for h in range(H):
+            kc = np.ascontiguousarray(k_codes[b, h].astype(np.float64).T)
+            for r0 in range(0, S, 1024):
+                r = rows[r0:r0 + 1024]
+                dots = q_codes[b, h, r].astype(np.float64) @ kc
+                sc = dots * sq_rows[b, h, r0:r0 + 1024, None] * sk_cols[b, h][None, :] * scale
+                m = sc.max(axis=1)
+                out[b, h, r0:r0 + 1024] = m + np.log(np.exp(sc - m[:, None]).sum(axis=1))
+    return out

@@ -160,6 +160,79 @@ def test_against_torch_sdpa_fp64():
     np.testing.assert_allclose(oracle.attention(q, k, v), ref, rtol=1e-11, atol=1e-12)
 
 
+def test_lse_brute_force_and_single_key():
+    rng = np.random.default_rng(31)
+    q, k = rng.standard_normal((1, 2, 4, 6)), rng.standard_normal((1, 2, 7, 6))
+    sc = 0.41
+    got = oracle.log_sum_exp(q, k, sc)
+    for h in range(2):
+        for i in range(4):
+            z = sum(math.exp(sc * sum(a * b for a, b in zip(q[0, h, i], kj))) for kj in k[0, h])
+            assert abs(got[0, h, i] - math.log(z)) < 1e-12
+    # one key: the normaliser is exp(s), lse = s exactly up to rounding of the dot product
+    k1 = k[:, :, :1]
+    np.testing.assert_allclose(oracle.log_sum_exp(q, k1, sc)[..., None],
+                               sc * q @ np.swapaxes(k1, -1, -2), rtol=0, atol=1e-13)
+
+
+def test_lse_matches_scipy_logsumexp_and_survives_huge_scores():
+    from scipy.special import logsumexp
+    rng = np.random.default_rng(32)
+    q, k = rng.standard_normal((2, 2, 9, 16)), rng.standard_normal((2, 2, 40, 16))
+    s = (q @ np.swapaxes(k, -1, -2)) * 0.25
+    np.testing.assert_allclose(oracle.log_sum_exp(q, k, 0.25), logsumexp(s, axis=-1),
+                               rtol=1e-13, atol=1e-13)
+    # scores near 2000 (exp overflows without the max shift): lse = 2000 + log(#equal maxima)
+    k2 = np.zeros((1, 1, 3, 1)); k2[0, 0, :, 0] = [2000.0, 2000.0, 0.0]
+    q2 = np.ones((1, 1, 1, 1))
+    assert abs(oracle.log_sum_exp(q2, k2, 1.0)[0, 0, 0] - (2000.0 + math.log(2.0))) < 1e-12
+
+
+def test_lse_merges_attention_over_disjoint_key_sets():
+    # the property a sequence split over devices relies on: results over key halves A and B
+    # combine into the full result through their log-sum-exps
+    rng = np.random.default_rng(33)
+    q = rng.standard_normal((1, 3, 11, 8))
+    k = rng.standard_normal((1, 3, 30, 8)) * 2
+    v = rng.standard_normal((1, 3, 30, 5))
+    ka, kb, va, vb = k[:, :, :13], k[:, :, 13:], v[:, :, :13], v[:, :, 13:]
+    la, lb = oracle.log_sum_exp(q, ka), oracle.log_sum_exp(q, kb)
+    oa, ob = oracle.attention(q, ka, va), oracle.attention(q, kb, vb)
+    lse = np.logaddexp(la, lb)
+    np.testing.assert_allclose(lse, oracle.log_sum_exp(q, k), rtol=1e-13, atol=1e-13)
+    merged = np.exp(la - lse)[..., None] * oa + np.exp(lb - lse)[..., None] * ob
+    np.testing.assert_allclose(merged, oracle.attention(q, k, v), rtol=1e-12, atol=1e-13)
+
+
+def test_lse_shifts_with_a_common_score_offset():
+    # adding u to every key with q . u = c for one query row shifts that row's lse by scale * c
+    rng = np.random.default_rng(34)
+    q = rng.standard_normal((1, 1, 1, 8))
+    k = rng.standard_normal((1, 1, 25, 8))
+    u = q[0, 0, 0] * (3.0 / float(q[0, 0, 0] @ q[0, 0, 0]))   # q . u = 3
+    got = oracle.log_sum_exp(q, k + u, 0.5) - oracle.log_sum_exp(q, k, 0.5)
+    assert abs(got[0, 0, 0] - 1.5) < 1e-12
+
+
+def test_int8_lse_reduces_to_exact_lse_when_codes_are_the_values():
+    # integer Q, K on the code grid with unit scales: the int8 normaliser equals the exact one
+    rng = np.random.default_rng(35)
+    qc = rng.integers(-127, 128, (1, 2, 130, 32)).astype(np.int8)
+    kc = rng.integers(-127, 128, (1, 2, 70, 32)).astype(np.int8)
+    qs = np.ones((1, 2, 2), np.float32)
+    ks = np.ones((1, 2, 2), np.float32)
+    sc = 1.0 / 4096
+    got = oracle.log_sum_exp_int8(qc, qs, kc, ks, sc)
+    np.testing.assert_allclose(got, oracle.log_sum_exp(qc.astype(np.float64), kc.astype(np.float64), sc),
+                               rtol=1e-13, atol=1e-13)
+    # per-block scales act on their own tokens: doubling k_scale of block 1 equals doubling
+    # those keys' codes in the exact formula
+    ks2 = ks.copy(); ks2[:, :, 1] = 2.0
+    k_eff = kc.astype(np.float64); k_eff[:, :, 64:] *= 2.0
+    np.testing.assert_allclose(oracle.log_sum_exp_int8(qc, qs, kc, ks2, sc),
+                               oracle.log_sum_exp(qc.astype(np.float64), k_eff, sc), rtol=1e-13, atol=1e-13)
+
+
 def test_attention_rows_equal_full_rows():
     rng = np.random.default_rng(9)
     q = rng.standard_normal((1, 2, 2100, 8))
