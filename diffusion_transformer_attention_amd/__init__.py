@@ -13,6 +13,12 @@ Entry points (same names as the C ABI in include/ditattn.h):
   resid_rel_l1(a, b, out=None, workspace=None) -> out (fp32 device scalar, shape [1])
 
 plus helpers for the int8 workspace (int8qk_workspace, int8qk_views) and the library path.
+
+The attention calls also take strided [B, H, S, D] views (channel axis contiguous), for
+instance q.transpose(1, 2) of a [B, S, H, D] tensor or a slice of a fused QKV projection, an
+output dtype (out_dtype=torch.bfloat16, or a bf16 `out`) and `lse` (a fp32 [B, H, S] tensor,
+or lse=True to allocate one), which return (out, lse); those go through the C ABI's
+attn_fwd_bf16_ex / attn_fwd_int8qk_ex, the plain contiguous fp32 case through the plain calls.
 """
 from __future__ import annotations
 
@@ -58,6 +64,11 @@ def lib() -> ctypes.CDLL:
     L.attn_int8qk_workspace_offsets.restype = sz
     L.attn_fwd_int8qk.argtypes = [vp, vp, vp, vp, i, i, i, i, f, vp, sz, vp]
     L.attn_fwd_int8qk.restype = i
+    p64 = ctypes.POINTER(i64)
+    L.attn_fwd_bf16_ex.argtypes = [vp, vp, vp, vp, i, vp, p64, i, i, i, i, f, vp]
+    L.attn_fwd_bf16_ex.restype = i
+    L.attn_fwd_int8qk_ex.argtypes = [vp, vp, vp, vp, i, vp, p64, i, i, i, i, f, vp, sz, vp]
+    L.attn_fwd_int8qk_ex.restype = i
     L.resid_rel_l1_workspace_bytes.argtypes = [i64]
     L.resid_rel_l1_workspace_bytes.restype = sz
     L.resid_rel_l1.argtypes = [vp, vp, i64, vp, vp, sz, vp]
@@ -81,30 +92,76 @@ def _ptr(t):
     return ctypes.c_void_p(t.data_ptr()) if t is not None else None
 
 
+OUT_F32, OUT_BF16 = 0, 1
+
+
 def _qkv_shape(q, k, v):
     for name, t in (("q", q), ("k", k), ("v", v)):
-        if not t.is_cuda or t.dtype != torch.bfloat16 or not t.is_contiguous() or t.dim() != 4:
-            raise ValueError(f"{name} must be a contiguous 4-D bf16 CUDA tensor [B, H, S, D]")
+        if not t.is_cuda or t.dtype != torch.bfloat16 or t.dim() != 4 or t.stride(3) != 1:
+            raise ValueError(f"{name} must be a 4-D bf16 CUDA tensor [B, H, S, D] "
+                             "with a contiguous channel axis")
     if q.shape != k.shape or q.shape != v.shape:
         raise ValueError("q, k, v must have the same shape [B, H, S, D]")
+    if q.device != k.device or q.device != v.device:
+        raise ValueError("q, k, v must be on the same device")
     return tuple(int(x) for x in q.shape)
 
 
-def _out(out, shape, device):
-    if out is None:
-        return torch.empty(shape, dtype=torch.float32, device=device)
-    if out.dtype != torch.float32 or not out.is_contiguous() or tuple(out.shape) != tuple(shape):
-        raise ValueError(f"out must be a contiguous fp32 tensor of shape {tuple(shape)}")
-    return out
+def _bhs_strides(t):
+    """(batch, head, token) element strides; a size-1 axis is never stepped, so it gets 0."""
+    return [0 if t.shape[d] == 1 else int(t.stride(d)) for d in range(3)]
 
 
-def attn_fwd_bf16(q, k, v, out=None, scale=None):
-    """Exact attention O = softmax(Q K^T * scale) V; q, k, v bf16 [B,H,S,D] -> fp32 [B,H,S,D]."""
+def _attn_args(q, k, v, out, out_dtype, lse):
+    """Shape, output tensor, lse tensor (or None) and whether the extended call is needed."""
     B, H, S, D = _qkv_shape(q, k, v)
+    if out is not None:
+        if out.dtype not in (torch.float32, torch.bfloat16) or tuple(out.shape) != (B, H, S, D) \
+                or out.stride(3) != 1 or out.device != q.device:
+            raise ValueError(f"out must be a fp32 or bf16 tensor of shape {(B, H, S, D)} on "
+                             "q's device with a contiguous channel axis")
+        if out_dtype is not None and out.dtype != out_dtype:
+            raise ValueError("out_dtype differs from out.dtype")
+    else:
+        dt = torch.float32 if out_dtype is None else out_dtype
+        if dt not in (torch.float32, torch.bfloat16):
+            raise ValueError("out_dtype must be torch.float32 or torch.bfloat16")
+        if q.stride(1) < q.stride(2):   # heads interleaved per token: keep q's [B, S, H, D] order
+            out = torch.empty((B, S, H, D), dtype=dt, device=q.device).transpose(1, 2)
+        else:
+            out = torch.empty((B, H, S, D), dtype=dt, device=q.device)
+    if lse is True:
+        lse = torch.empty((B, H, S), dtype=torch.float32, device=q.device)
+    elif lse is False:
+        lse = None
+    if lse is not None and (lse.dtype != torch.float32 or tuple(lse.shape) != (B, H, S)
+                            or not lse.is_contiguous() or lse.device != q.device):
+        raise ValueError(f"lse must be a contiguous fp32 tensor of shape {(B, H, S)}")
+    plain = (lse is None and out.dtype == torch.float32
+             and all(t.is_contiguous() for t in (q, k, v, out)))
+    return (B, H, S, D), out, lse, plain
+
+
+def _strides_arg(q, k, v, out):
+    return (ctypes.c_int64 * 12)(*(_bhs_strides(q) + _bhs_strides(k) + _bhs_strides(v)
+                                   + _bhs_strides(out)))
+
+
+def attn_fwd_bf16(q, k, v, out=None, scale=None, *, out_dtype=None, lse=None):
+    """Exact attention O = softmax(Q K^T * scale) V on bf16 [B,H,S,D] views.
+
+    Returns out (fp32 unless out_dtype / out say bf16), or (out, lse) when lse is given."""
+    (B, H, S, D), out, lse_t, plain = _attn_args(q, k, v, out, out_dtype, lse)
     scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
-    out = _out(out, (B, H, S, D), q.device)
-    _check(lib().attn_fwd_bf16(_ptr(q), _ptr(k), _ptr(v), _ptr(out), B, H, S, D, scale, _stream(q)))
-    return out
+    if plain:
+        _check(lib().attn_fwd_bf16(_ptr(q), _ptr(k), _ptr(v), _ptr(out), B, H, S, D, scale,
+                                   _stream(q)))
+    else:
+        _check(lib().attn_fwd_bf16_ex(
+            _ptr(q), _ptr(k), _ptr(v), _ptr(out),
+            OUT_BF16 if out.dtype == torch.bfloat16 else OUT_F32, _ptr(lse_t),
+            _strides_arg(q, k, v, out), B, H, S, D, scale, _stream(q)))
+    return out if lse_t is None else (out, lse_t)
 
 
 def int8qk_workspace_bytes(B, H, S, D) -> int:
@@ -138,18 +195,26 @@ def int8qk_views(workspace: torch.Tensor, B, H, S, D) -> dict:
             "k_codes": seg(4, torch.int8, (B, H, S, D))}
 
 
-def attn_fwd_int8qk(q, k, v, out=None, scale=None, workspace=None):
-    """int8-QK attention (K smoothed by its channel mean, per-block int8 Q/K, bf16 PV)."""
-    B, H, S, D = _qkv_shape(q, k, v)
+def attn_fwd_int8qk(q, k, v, out=None, scale=None, workspace=None, *, out_dtype=None, lse=None):
+    """int8-QK attention (K smoothed by its channel mean, per-block int8 Q/K, bf16 PV).
+
+    Arguments and result as attn_fwd_bf16; lse is that of the quantized scores."""
+    (B, H, S, D), out, lse_t, plain = _attn_args(q, k, v, out, out_dtype, lse)
     scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
-    out = _out(out, (B, H, S, D), q.device)
     if workspace is None:
         workspace = int8qk_workspace(B, H, S, D, q.device)
     if workspace.dtype != torch.uint8 or not workspace.is_cuda or not workspace.is_contiguous():
         raise ValueError("workspace must be a contiguous uint8 CUDA tensor")
-    _check(lib().attn_fwd_int8qk(_ptr(q), _ptr(k), _ptr(v), _ptr(out), B, H, S, D, scale,
-                                 _ptr(workspace), workspace.numel(), _stream(q)))
-    return out
+    if plain:
+        _check(lib().attn_fwd_int8qk(_ptr(q), _ptr(k), _ptr(v), _ptr(out), B, H, S, D, scale,
+                                     _ptr(workspace), workspace.numel(), _stream(q)))
+    else:
+        _check(lib().attn_fwd_int8qk_ex(
+            _ptr(q), _ptr(k), _ptr(v), _ptr(out),
+            OUT_BF16 if out.dtype == torch.bfloat16 else OUT_F32, _ptr(lse_t),
+            _strides_arg(q, k, v, out), B, H, S, D, scale, _ptr(workspace), workspace.numel(),
+            _stream(q)))
+    return out if lse_t is None else (out, lse_t)
 
 
 def rel_l1_workspace_bytes(n: int) -> int:

@@ -50,6 +50,7 @@ namespace {
 constexpr int kQBlock = 128;    // int8 Q quantization block (tokens)
 constexpr int kBK = 64;         // keys per tile (= int8 K block)
 constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kLazyW = 256.0f;  // 2^8: largest weight (and lane weight sum) kept as it is
 // 1.5 * 2^23: every fp32 in [2^23, 2^24) is an integer and consecutive integers have
 // consecutive bit patterns, so bits(kBiasF) + n read as fp32 is kBiasF + n for |n| < 2^22.
@@ -104,12 +105,31 @@ __device__ __forceinline__ int vswz(int row, int ch) {
 // An empty asm that the compiler must assume redefines x (a VGPR value).
 __device__ __forceinline__ void opaque(uint32_t& x) { asm volatile("" : "+v"(x)); }
 
+// Sizes and strides of one call (passed by value into the kernel's scalar argument segment).
+// Strides are in elements of the respective tensor; the channel axis is contiguous.  The
+// pointers stay separate __restrict__ arguments: only then may the per-tile K scale be read
+// with a scalar load, which does not wait for the K/V tile copies in flight.
+struct KArgs {
+  int64_t qsb, qsh, qss, ksb, ksh, kss, vsb, vsh, vss, osb, osh, oss;
+  int H, S, n_qt;
+  float c;                 // scale * log2(e)
+  int o_bf16;
+};
+
+// q, k: bf16 Q and K, or the int8 codes; v: bf16 V; o: fp32 or bf16 O; lse: fp32 [B, H, S]
+// natural-log normalisers, or null; q_scale / k_scale: the int8 path's per-block scales.
+// At D = 64 the wave count per SIMD is capped at two as well: one 8-wave workgroup per CU is
+// the design and a third wave slot could not hold a second workgroup, yet aiming for three
+// squeezes the kernel into 168 VGPRs and serialises its K fragment reads behind the products.
+// (At D = 128 the cap changes nothing but the instruction schedule, measurably for the worse.)
 template <int D, bool INT8, int NW>
-__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2)))
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, D == 64 ? 2 : 8)))
 void attn_fwd_kernel(const uint8_t* __restrict__ qp, const uint8_t* __restrict__ kp,
-                     const uint8_t* __restrict__ vp, float* __restrict__ op,
-                     const float* __restrict__ q_scale, const float* __restrict__ k_scale,
-                     int S, int n_qt, float c) {
+                     const uint8_t* __restrict__ vp, uint8_t* __restrict__ op,
+                     float* __restrict__ lse, const float* __restrict__ q_scale,
+                     const float* __restrict__ k_scale, const KArgs a) {
+  const int S = a.S, n_qt = a.n_qt;
+  const float c = a.c;
   using T = Tile<D, INT8, NW>;
   constexpr int kThreads = T::NT;
   constexpr int kBQ = T::BQ;
@@ -136,16 +156,17 @@ void attn_fwd_kernel(const uint8_t* __restrict__ qp, const uint8_t* __restrict__
   const int bh = L / n_qt;
   const int qt = L - bh * n_qt;
 
-  const size_t head = (size_t)bh * (size_t)S * D;  // element offset of this (b, h)
-  const uint8_t* kh = kp + head * EB;
-  const uint8_t* vh = vp + head * 2;
+  const int bb = bh / a.H, hd = bh - bb * a.H;
+  const uint8_t* kh = kp + (bb * a.ksb + hd * a.ksh) * EB;   // first key row of this (b, h)
+  const uint8_t* vh = vp + (bb * a.vsb + hd * a.vsh) * 2;
+  const int64_t krs = a.kss * EB, vrs = a.vss * 2;            // bytes between key / value rows
   const int nkt = (S + kBK - 1) / kBK;
 
   // ---- Q fragment: B operand; lane holds query q, bytes [32f + 16hh, +16) of its row -------
   const int q = qt * kBQ + wave * 32 + l32;
   u32x4 qf[T::NQF];
   {
-    const uint8_t* qrow = qp + (head + (size_t)min(q, S - 1) * D) * EB;
+    const uint8_t* qrow = qp + (bb * a.qsb + hd * a.qsh + (int64_t)min(q, S - 1) * a.qss) * EB;
 #pragma unroll
     for (int f = 0; f < T::NQF; ++f) {
       const u32x4 x = *reinterpret_cast<const u32x4*>(qrow + f * 32 + hh * 16);
@@ -174,21 +195,28 @@ void attn_fwd_kernel(const uint8_t* __restrict__ qp, const uint8_t* __restrict__
   for (int r = 0; r < T::KLD; ++r) {
     const int p = r * kThreads + tid;
     const int key = p / T::KCH, pch = p % T::KCH;
-    kofl[r] = key * T::KROW + kswz<D, INT8>(key, pch) * 16;
+    kofl[r] = (uint32_t)(key * krs) + kswz<D, INT8>(key, pch) * 16;
   }
 #pragma unroll
   for (int r = 0; r < T::VLD; ++r) {
     const int p = r * kThreads + tid;
     const int key = p / T::VCH, pch = p % T::VCH;
-    vofl[r] = key * T::VROW + vswz<D>(key, pch) * 16;
+    vofl[r] = (uint32_t)(key * vrs) + vswz<D>(key, pch) * 16;
   }
-  // first row of tile kt (uniform); S >= kBK whenever more than one tile exists
-  auto tile_row = [&](int kt) { return min(kt * kBK, S - kBK); };
+  // First row of tile kt: kt * kBK, except a ragged last tile, which starts at S - kBK
+  // (S >= kBK whenever more than one tile exists).  Tiles of K and of V are each loaded once,
+  // in order, so their base addresses advance by one tile per load (uniform, in SGPRs).
+  const uint8_t* k_next = kh;
+  const uint8_t* v_next = vh;
+  const uint8_t* const k_last = kh + (int64_t)max(S - kBK, 0) * krs;
+  const uint8_t* const v_last = vh + (int64_t)max(S - kBK, 0) * vrs;
+  const int64_t k_step = kBK * krs, v_step = kBK * vrs;
   // The offsets are redefined (by an empty asm) at the top of every loop iteration, so their
   // zero extension cannot be hoisted out of the loop and each address is selected as scalar
   // base + 32-bit vector offset (the global "saddr" form), not a 64-bit VALU add.
   auto load_k = [&](int kt, uint8_t* dst) {
-    const uint8_t* tb = kh + (size_t)tile_row(kt) * T::KROW;
+    const uint8_t* tb = kt == nkt - 1 ? k_last : k_next;
+    k_next += k_step;
     if (T::KPART && wave_u * 64 >= T::KBYTES / 16) return;  // this wave has no K slot
 #pragma unroll
     for (int r = 0; r < T::KLD; ++r) {
@@ -198,7 +226,8 @@ void attn_fwd_kernel(const uint8_t* __restrict__ qp, const uint8_t* __restrict__
     }
   };
   auto load_v = [&](int kt, uint8_t* dst) {
-    const uint8_t* tb = vh + (size_t)tile_row(kt) * T::VROW;
+    const uint8_t* tb = kt == nkt - 1 ? v_last : v_next;
+    v_next += v_step;
 #pragma unroll
     for (int r = 0; r < T::VLD; ++r) {
       const uint32_t off = vofl[r];
@@ -212,14 +241,14 @@ void attn_fwd_kernel(const uint8_t* __restrict__ qp, const uint8_t* __restrict__
       if (T::KPART && wave_u * 64 >= T::KBYTES / 16) break;
       const int p = r * kThreads + tid;
       const int key = p / T::KCH, pch = p % T::KCH;
-      const uint32_t off = min(key, S - 1) * T::KROW + kswz<D, INT8>(key, pch) * 16;
+      const uint32_t off = (uint32_t)(min(key, S - 1) * krs) + kswz<D, INT8>(key, pch) * 16;
       __builtin_amdgcn_global_load_lds(kh + off, (lds_void*)(kdst + (r * kThreads + wave_u * 64) * 16), 16, 0, 0);
     }
 #pragma unroll
     for (int r = 0; r < T::VLD; ++r) {
       const int p = r * kThreads + tid;
       const int key = p / T::VCH, pch = p % T::VCH;
-      const uint32_t off = min(key, S - 1) * T::VROW + vswz<D>(key, pch) * 16;
+      const uint32_t off = (uint32_t)(min(key, S - 1) * vrs) + vswz<D>(key, pch) * 16;
       __builtin_amdgcn_global_load_lds(vh + off, (lds_void*)(vdst + (r * kThreads + wave_u * 64) * 16), 16, 0, 0);
     }
   };
@@ -298,7 +327,7 @@ void attn_fwd_kernel(const uint8_t* __restrict__ qp, const uint8_t* __restrict__
   // range is [lo, hi); the empty asm keeps the comparisons inside the rarely taken branch.
   auto mask_tile = [&](int jt, float (&s)[32]) __attribute__((always_inline)) {
     if (jt == nkt - 1 && (S % kBK) != 0) {
-      const int t0 = tile_row(jt) > 0 ? tile_row(jt) : 0;
+      const int t0 = max(S - kBK, 0);  // the tile's first row
       int lo = jt * kBK - t0 - 4 * hh, hi = S - t0 - 4 * hh;
       asm volatile("" : "+v"(lo), "+v"(hi));
 #pragma unroll
@@ -445,30 +474,58 @@ void attn_fwd_kernel(const uint8_t* __restrict__ qp, const uint8_t* __restrict__
   }
   if (j < nkt) stage(j, std::integral_constant<int, 0>{}, sb, sa, pa, pbb);
 
-  // ---- epilogue: O = O_acc / l, fp32 ---------------------------------------------------
-  const float inv = 1.f / xor32_sum(l_run);
+  // ---- epilogue: O = O_acc / l (fp32 or bf16), and optionally the row's log-sum-exp ------
+  const float l_tot = xor32_sum(l_run);
+  const float inv = 1.f / l_tot;
   if (q < S) {
-    float* orow = op + head + (size_t)q * D;
+    const int64_t orow = bb * a.osb + hd * a.osh + (int64_t)q * a.oss;  // element offset
+    if (a.o_bf16) {
+      uint16_t* o16 = reinterpret_cast<uint16_t*>(op) + orow;
 #pragma unroll
-    for (int db = 0; db < T::NDB; ++db)
+      for (int db = 0; db < T::NDB; ++db)
 #pragma unroll
-      for (int jj = 0; jj < 4; ++jj) {
-        const f32x4 o4 = {oacc[db][4 * jj] * inv, oacc[db][4 * jj + 1] * inv,
-                          oacc[db][4 * jj + 2] * inv, oacc[db][4 * jj + 3] * inv};
-        *reinterpret_cast<f32x4*>(orow + db * 32 + 8 * jj + 4 * hh) = o4;
-      }
+        for (int jj = 0; jj < 4; ++jj) {
+          const bf16x2 lo = {(__bf16)(oacc[db][4 * jj] * inv), (__bf16)(oacc[db][4 * jj + 1] * inv)};
+          const bf16x2 hi = {(__bf16)(oacc[db][4 * jj + 2] * inv), (__bf16)(oacc[db][4 * jj + 3] * inv)};
+          *reinterpret_cast<u32x2*>(o16 + db * 32 + 8 * jj + 4 * hh) =
+              u32x2{__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi)};
+        }
+    } else {
+      float* o32 = reinterpret_cast<float*>(op) + orow;
+#pragma unroll
+      for (int db = 0; db < T::NDB; ++db)
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+          const f32x4 o4 = {oacc[db][4 * jj] * inv, oacc[db][4 * jj + 1] * inv,
+                            oacc[db][4 * jj + 2] * inv, oacc[db][4 * jj + 3] * inv};
+          *reinterpret_cast<f32x4*>(o32 + db * 32 + 8 * jj + 4 * hh) = o4;
+        }
+    }
+    // log sum_j exp(scale * s_j) = (m + log2 l) * ln 2: the weights are 2^(scale log2e s - m)
+    if (lse != nullptr && hh == 0)
+      lse[(int64_t)bh * S + q] = (m_run + __builtin_amdgcn_logf(l_tot)) * kLn2;
   }
 }
 
 template <int D, bool INT8, int NW>
-hipError_t launch(const void* q, const void* k, const void* v, float* o, const float* qs,
-                  const float* ks, int B, int H, int S, float scale, hipStream_t stream) {
+hipError_t launch(const AttnCall& ac, const void* q, Strides qs, const void* k, Strides ks,
+                  const float* q_scale, const float* k_scale, hipStream_t stream) {
   using T = Tile<D, INT8, NW>;
-  const int n_qt = (S + T::BQ - 1) / T::BQ;
-  const long long nwg = (long long)B * H * n_qt;
+  KArgs a;
+  a.qsb = qs.b; a.qsh = qs.h; a.qss = qs.s;
+  a.ksb = ks.b; a.ksh = ks.h; a.kss = ks.s;
+  a.vsb = ac.vs.b; a.vsh = ac.vs.h; a.vss = ac.vs.s;
+  a.osb = ac.os.b; a.osh = ac.os.h; a.oss = ac.os.s;
+  a.H = ac.H;
+  a.S = ac.S;
+  a.n_qt = (ac.S + T::BQ - 1) / T::BQ;
+  a.c = ac.scale * kLog2e;
+  a.o_bf16 = ac.o_bf16 ? 1 : 0;
+  const long long nwg = (long long)ac.B * ac.H * a.n_qt;
   hipLaunchKernelGGL((attn_fwd_kernel<D, INT8, NW>), dim3((unsigned)nwg), dim3(T::NT), 0, stream,
                      static_cast<const uint8_t*>(q), static_cast<const uint8_t*>(k),
-                     static_cast<const uint8_t*>(v), o, qs, ks, S, n_qt, scale * kLog2e);
+                     static_cast<const uint8_t*>(ac.v), static_cast<uint8_t*>(ac.o), ac.lse,
+                     q_scale, k_scale, a);
   return hipGetLastError();
 }
 
@@ -478,18 +535,20 @@ hipError_t launch(const void* q, const void* k, const void* v, float* o, const f
 // SIMD) share each K/V tile twice as widely as four, halving the L2 -> LDS traffic per flop;
 // measured 4-6% faster on both variants at S = 4608 and S = 118800.
 constexpr int kWaves = 8;
-hipError_t launch_attn_bf16(const void* q, const void* k, const void* v, float* o, int B, int H,
-                            int S, int D, float scale, hipStream_t stream) {
-  if (D == 64) return launch<64, false, kWaves>(q, k, v, o, nullptr, nullptr, B, H, S, scale, stream);
-  return launch<128, false, kWaves>(q, k, v, o, nullptr, nullptr, B, H, S, scale, stream);
+
+hipError_t launch_attn_bf16(const AttnCall& ac, hipStream_t stream) {
+  if (ac.D == 64)
+    return launch<64, false, kWaves>(ac, ac.q, ac.qs, ac.k, ac.ks, nullptr, nullptr, stream);
+  return launch<128, false, kWaves>(ac, ac.q, ac.qs, ac.k, ac.ks, nullptr, nullptr, stream);
 }
 
-hipError_t launch_attn_int8(const void* q_codes, const void* k_codes, const void* v, float* o,
-                            const float* q_scale, const float* k_scale, int B, int H, int S,
-                            int D, float scale, hipStream_t stream) {
-  if (D == 64)
-    return launch<64, true, kWaves>(q_codes, k_codes, v, o, q_scale, k_scale, B, H, S, scale, stream);
-  return launch<128, true, kWaves>(q_codes, k_codes, v, o, q_scale, k_scale, B, H, S, scale, stream);
+hipError_t launch_attn_int8(const AttnCall& ac, const int8_t* q_codes, const int8_t* k_codes,
+                            const float* q_scale, const float* k_scale, hipStream_t stream) {
+  // the codes are the prepass's own contiguous [B, H, S, D] buffers
+  const Strides cs{(int64_t)ac.H * ac.S * ac.D, (int64_t)ac.S * ac.D, ac.D};
+  if (ac.D == 64)
+    return launch<64, true, kWaves>(ac, q_codes, cs, k_codes, cs, q_scale, k_scale, stream);
+  return launch<128, true, kWaves>(ac, q_codes, cs, k_codes, cs, q_scale, k_scale, stream);
 }
 
 }  // namespace ditattn

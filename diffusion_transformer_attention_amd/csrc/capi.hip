@@ -38,6 +38,79 @@ int check_attn_args(const void* q, const void* k, const void* v, const float* o,
 
 int status_of(hipError_t e) { return e == hipSuccess ? DITATTN_OK : DITATTN_EHIP; }
 
+// Strides of the extended calls: non-negative, 16-byte multiples, token strides of the inputs
+// small enough for the kernels' 32-bit per-row offsets within a 64-row tile.
+bool strides_ok(const int64_t* st, bool o_bf16) {
+  for (int t = 0; t < 4; ++t) {
+    const int64_t unit = (t == 3 && !o_bf16) ? 4 : 8;  // elements per 16 bytes
+    for (int a = 0; a < 3; ++a) {
+      const int64_t x = st[3 * t + a];
+      if (x < 0 || x % unit != 0) return false;
+    }
+    if (t < 3 && st[3 * t + 2] >= (int64_t(1) << 24)) return false;
+  }
+  return true;
+}
+
+int check_ex_args(const void* q, const void* k, const void* v, const void* o, int out_dtype,
+                  const float* lse, const int64_t* strides, int B, int H, int S, int D,
+                  float scale) {
+  if (!q || !k || !v || !o || !strides) return DITATTN_EINVAL;
+  if (out_dtype != DITATTN_OUT_F32 && out_dtype != DITATTN_OUT_BF16) return DITATTN_EINVAL;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16)) return DITATTN_EINVAL;
+  if (o == q || o == k || o == v) return DITATTN_EINVAL;
+  if (lse && (!aligned(lse, 4) || static_cast<const void*>(lse) == o ||
+              static_cast<const void*>(lse) == q || static_cast<const void*>(lse) == k ||
+              static_cast<const void*>(lse) == v))
+    return DITATTN_EINVAL;
+  if (!(scale > 0.f) || !isfinite(scale)) return DITATTN_EINVAL;
+  const int st = check_attn_shape(B, H, S, D);
+  if (st != DITATTN_OK) return st;
+  if (!strides_ok(strides, out_dtype == DITATTN_OUT_BF16)) return DITATTN_EINVAL;
+  return DITATTN_OK;
+}
+
+ditattn::AttnCall make_call(const void* q, const void* k, const void* v, void* o, bool o_bf16,
+                            float* lse, const int64_t* st, int B, int H, int S, int D,
+                            float scale) {
+  ditattn::AttnCall ac;
+  ac.q = q; ac.k = k; ac.v = v; ac.o = o; ac.o_bf16 = o_bf16; ac.lse = lse;
+  ac.qs = {st[0], st[1], st[2]};
+  ac.ks = {st[3], st[4], st[5]};
+  ac.vs = {st[6], st[7], st[8]};
+  ac.os = {st[9], st[10], st[11]};
+  ac.B = B; ac.H = H; ac.S = S; ac.D = D; ac.scale = scale;
+  return ac;
+}
+
+void contiguous_strides(int H, int S, int D, int64_t st[12]) {
+  for (int t = 0; t < 4; ++t) {
+    st[3 * t] = (int64_t)H * S * D;
+    st[3 * t + 1] = (int64_t)S * D;
+    st[3 * t + 2] = D;
+  }
+}
+
+// The int8 path after validation: workspace check, prepass, attention.
+int int8qk_run(const ditattn::AttnCall& ac, void* workspace, size_t workspace_bytes,
+               hipStream_t s) {
+  size_t off[6];
+  const size_t need = attn_int8qk_workspace_offsets(ac.B, ac.H, ac.S, ac.D, off);
+  if (!workspace || !aligned(workspace, kSegAlign) || workspace_bytes < need) return DITATTN_EWORKSPACE;
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  float* k_mean = reinterpret_cast<float*>(ws + off[0]);
+  float* q_scale = reinterpret_cast<float*>(ws + off[1]);
+  float* k_scale = reinterpret_cast<float*>(ws + off[2]);
+  int8_t* q_codes = reinterpret_cast<int8_t*>(ws + off[3]);
+  int8_t* k_codes = reinterpret_cast<int8_t*>(ws + off[4]);
+  double* partial = reinterpret_cast<double*>(ws + off[5]);
+  const hipError_t e = ditattn::launch_prepass(ac.q, ac.qs, ac.k, ac.ks, k_mean, partial, q_codes,
+                                               k_codes, q_scale, k_scale, ac.B, ac.H, ac.S, ac.D,
+                                               s);
+  if (e != hipSuccess) return DITATTN_EHIP;
+  return status_of(ditattn::launch_attn_int8(ac, q_codes, k_codes, q_scale, k_scale, s));
+}
+
 }  // namespace
 
 extern "C" {
@@ -57,8 +130,21 @@ int attn_fwd_bf16(const void* q, const void* k, const void* v, float* o, int B, 
                   int D, float scale, void* stream) {
   const int st = check_attn_args(q, k, v, o, B, H, S, D, scale);
   if (st != DITATTN_OK) return st;
-  return status_of(ditattn::launch_attn_bf16(q, k, v, o, B, H, S, D, scale,
-                                             static_cast<hipStream_t>(stream)));
+  int64_t strides[12];
+  contiguous_strides(H, S, D, strides);
+  return status_of(ditattn::launch_attn_bf16(
+      make_call(q, k, v, o, false, nullptr, strides, B, H, S, D, scale),
+      static_cast<hipStream_t>(stream)));
+}
+
+int attn_fwd_bf16_ex(const void* q, const void* k, const void* v, void* o, int out_dtype,
+                     float* lse, const int64_t* strides, int B, int H, int S, int D, float scale,
+                     void* stream) {
+  const int st = check_ex_args(q, k, v, o, out_dtype, lse, strides, B, H, S, D, scale);
+  if (st != DITATTN_OK) return st;
+  return status_of(ditattn::launch_attn_bf16(
+      make_call(q, k, v, o, out_dtype == DITATTN_OUT_BF16, lse, strides, B, H, S, D, scale),
+      static_cast<hipStream_t>(stream)));
 }
 
 size_t attn_int8qk_workspace_offsets(int B, int H, int S, int D, size_t offsets[6]) {
@@ -88,24 +174,20 @@ int attn_fwd_int8qk(const void* q, const void* k, const void* v, float* o, int B
                     int D, float scale, void* workspace, size_t workspace_bytes, void* stream) {
   const int st = check_attn_args(q, k, v, o, B, H, S, D, scale);
   if (st != DITATTN_OK) return st;
-  size_t off[6];
-  const size_t need = attn_int8qk_workspace_offsets(B, H, S, D, off);
-  if (!workspace || !aligned(workspace, kSegAlign) || workspace_bytes < need) return DITATTN_EWORKSPACE;
+  int64_t strides[12];
+  contiguous_strides(H, S, D, strides);
+  return int8qk_run(make_call(q, k, v, o, false, nullptr, strides, B, H, S, D, scale), workspace,
+                    workspace_bytes, static_cast<hipStream_t>(stream));
+}
 
-  uint8_t* ws = static_cast<uint8_t*>(workspace);
-  float* k_mean = reinterpret_cast<float*>(ws + off[0]);
-  float* q_scale = reinterpret_cast<float*>(ws + off[1]);
-  float* k_scale = reinterpret_cast<float*>(ws + off[2]);
-  int8_t* q_codes = reinterpret_cast<int8_t*>(ws + off[3]);
-  int8_t* k_codes = reinterpret_cast<int8_t*>(ws + off[4]);
-  double* partial = reinterpret_cast<double*>(ws + off[5]);
-  hipStream_t s = static_cast<hipStream_t>(stream);
-
-  const hipError_t e = ditattn::launch_prepass(q, k, k_mean, partial, q_codes, k_codes, q_scale,
-                                               k_scale, B, H, S, D, s);
-  if (e != hipSuccess) return DITATTN_EHIP;
-  return status_of(ditattn::launch_attn_int8(q_codes, k_codes, v, o, q_scale, k_scale, B, H, S,
-                                             D, scale, s));
+int attn_fwd_int8qk_ex(const void* q, const void* k, const void* v, void* o, int out_dtype,
+                       float* lse, const int64_t* strides, int B, int H, int S, int D,
+                       float scale, void* workspace, size_t workspace_bytes, void* stream) {
+  const int st = check_ex_args(q, k, v, o, out_dtype, lse, strides, B, H, S, D, scale);
+  if (st != DITATTN_OK) return st;
+  return int8qk_run(
+      make_call(q, k, v, o, out_dtype == DITATTN_OUT_BF16, lse, strides, B, H, S, D, scale),
+      workspace, workspace_bytes, static_cast<hipStream_t>(stream));
 }
 
 size_t resid_rel_l1_workspace_bytes(int64_t n) {

@@ -9,12 +9,30 @@
 
 namespace ditattn {
 
-hipError_t launch_attn_bf16(const void* q, const void* k, const void* v, float* o, int B, int H,
-                            int S, int D, float scale, hipStream_t stream);
+// Element strides of a [B, H, S, D] tensor view: batch, head, token.  The channel axis is
+// contiguous.
+struct Strides {
+  int64_t b, h, s;
+};
 
-hipError_t launch_attn_int8(const void* q_codes, const void* k_codes, const void* v, float* o,
-                            const float* q_scale, const float* k_scale, int B, int H, int S,
-                            int D, float scale, hipStream_t stream);
+// One attention call: q, k, v bf16 views, o fp32 or bf16 view, optional lse fp32 [B, H, S].
+struct AttnCall {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  bool o_bf16;
+  float* lse;
+  Strides qs, ks, vs, os;
+  int B, H, S, D;
+  float scale;
+};
+
+hipError_t launch_attn_bf16(const AttnCall& ac, hipStream_t stream);
+
+// The int8-QK attention on the prepass's contiguous codes and scales (V, O, lse from `ac`).
+hipError_t launch_attn_int8(const AttnCall& ac, const int8_t* q_codes, const int8_t* k_codes,
+                            const float* q_scale, const float* k_scale, hipStream_t stream);
 
 // Number of token chunks the K-mean partial pass splits each (b, h) into.
 int kmean_chunks(int B, int H, int S);
@@ -23,9 +41,9 @@ int kmean_chunks(int B, int H, int S);
 // fp32) and per-block int8 quantization of Q (128-token blocks) and of the mean-smoothed K
 // (64-token blocks).  Three launches: mean partial sums together with the Q blocks, the mean,
 // then the K blocks.  partial: scratch of B*H*kmean_chunks(B,H,S)*D double pairs.
-hipError_t launch_prepass(const void* q, const void* k, float* k_mean, double* partial,
-                          int8_t* q_codes, int8_t* k_codes, float* q_scale, float* k_scale, int B,
-                          int H, int S, int D, hipStream_t stream);
+hipError_t launch_prepass(const void* q, Strides qs, const void* k, Strides ks, float* k_mean,
+                          double* partial, int8_t* q_codes, int8_t* k_codes, float* q_scale,
+                          float* k_scale, int B, int H, int S, int D, hipStream_t stream);
 
 // Number of partial-sum workgroups the relative-L1 pass uses for n elements.
 int rel_l1_blocks(int64_t n);

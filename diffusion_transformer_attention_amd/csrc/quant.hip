@@ -26,7 +26,7 @@ constexpr int kThreads = 256;
 
 // ---- K channel mean: exact double-double partial sums over token chunks ------------------
 template <int D>
-__device__ __forceinline__ void kmean_partial(const uint16_t* __restrict__ k,
+__device__ __forceinline__ void kmean_partial(const uint16_t* __restrict__ k, Strides ks, int H,
                                               double* __restrict__ partial, int S, int nch,
                                               int rows_per, int id) {
   constexpr int TPR = D / 8;             // threads per token row (8 channels each)
@@ -40,7 +40,7 @@ __device__ __forceinline__ void kmean_partial(const uint16_t* __restrict__ k,
   const int cg = tid % TPR, rg = tid / TPR;
   const int r0 = chunk * rows_per;
   const int r1 = min(S, r0 + rows_per);
-  const uint16_t* kh = k + (size_t)bh * S * D;
+  const uint16_t* kh = k + (bh / H) * ks.b + (bh % H) * ks.h;
 
   DDSum acc[8];
   auto add_row = [&](const u32x4& x) {
@@ -57,11 +57,11 @@ __device__ __forceinline__ void kmean_partial(const uint16_t* __restrict__ k,
     u32x4 x[U];
 #pragma unroll
     for (int u = 0; u < U; ++u)
-      x[u] = *reinterpret_cast<const u32x4*>(kh + (size_t)(row + u * RPP) * D + cg * 8);
+      x[u] = *reinterpret_cast<const u32x4*>(kh + (int64_t)(row + u * RPP) * ks.s + cg * 8);
 #pragma unroll
     for (int u = 0; u < U; ++u) add_row(x[u]);
   }
-  for (; row < r1; row += RPP) add_row(*reinterpret_cast<const u32x4*>(kh + (size_t)row * D + cg * 8));
+  for (; row < r1; row += RPP) add_row(*reinterpret_cast<const u32x4*>(kh + (int64_t)row * ks.s + cg * 8));
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
     red_hi[tid][e] = acc[e].hi;
@@ -112,8 +112,11 @@ __global__ __launch_bounds__(kThreads) void kmean_final_kernel(const double* __r
 }
 
 // ---- per-block quantization --------------------------------------------------------------
+// One block of BT tokens of (b, h) = (bh / H, bh % H): x is read through its strides, the
+// codes are written to the contiguous [B, H, S, D] buffer.
 template <int D, int BT, bool SMOOTH>
-__device__ __forceinline__ void quant_block(const uint16_t* __restrict__ x, const float* __restrict__ mean,
+__device__ __forceinline__ void quant_block(const uint16_t* __restrict__ x, Strides xs, int H,
+                                            const float* __restrict__ mean,
                                             int8_t* __restrict__ codes, float* __restrict__ scale_out,
                                             int S, int bh, int blk) {
   constexpr int CPR = D / 8;                       // 16-byte chunks per token row
@@ -124,7 +127,8 @@ __device__ __forceinline__ void quant_block(const uint16_t* __restrict__ x, cons
   const int tid = threadIdx.x;
   const int t0 = blk * BT;
   const int nt = min(BT, S - t0);
-  const size_t base = ((size_t)bh * S + t0) * D;
+  const size_t base = ((size_t)bh * S + t0) * D;                            // codes
+  const uint16_t* xrow0 = x + (bh / H) * xs.b + (bh % H) * xs.h + (int64_t)t0 * xs.s;
 
   float v[NC][8];
   float amax = 0.f;
@@ -133,7 +137,7 @@ __device__ __forceinline__ void quant_block(const uint16_t* __restrict__ x, cons
     const int id = tid + r * kThreads;
     const int tok = id / CPR, ch = id % CPR;
     u32x4 w = u32x4{0u, 0u, 0u, 0u};
-    if (tok < nt) w = *reinterpret_cast<const u32x4*>(x + base + (size_t)tok * D + ch * 8);
+    if (tok < nt) w = *reinterpret_cast<const u32x4*>(xrow0 + (int64_t)tok * xs.s + ch * 8);
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       v[r][2 * e] = bf16lo(w[e]);
@@ -187,28 +191,30 @@ __device__ __forceinline__ void quant_block(const uint16_t* __restrict__ x, cons
 // the mean, the Q blocks (the remaining ids) in one launch.
 template <int D>
 __global__ __launch_bounds__(kThreads) void kmean_partial_quant_q_kernel(
-    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, double* __restrict__ partial,
-    int8_t* __restrict__ q_codes, float* __restrict__ q_scale, int S, int BH, int nch, int rows_per,
-    int nqb) {
+    const uint16_t* __restrict__ q, Strides qs, const uint16_t* __restrict__ k, Strides ks, int H,
+    double* __restrict__ partial, int8_t* __restrict__ q_codes, float* __restrict__ q_scale, int S,
+    int BH, int nch, int rows_per, int nqb) {
   const int id = blockIdx.x;
   if (id < BH * nch) {
-    kmean_partial<D>(k, partial, S, nch, rows_per, id);
+    kmean_partial<D>(k, ks, H, partial, S, nch, rows_per, id);
   } else {
     const int j = id - BH * nch;
     const int bh = j / nqb, blk = j - bh * nqb;
-    quant_block<D, 128, false>(q, nullptr, q_codes, q_scale + (size_t)bh * nqb + blk, S, bh, blk);
+    quant_block<D, 128, false>(q, qs, H, nullptr, q_codes, q_scale + (size_t)bh * nqb + blk, S, bh,
+                               blk);
   }
 }
 
 // Last pass: the K blocks, smoothed by the finished mean.
 template <int D>
 __global__ __launch_bounds__(kThreads) void quant_k_kernel(const uint16_t* __restrict__ k,
+                                                           Strides ks, int H,
                                                            const float* __restrict__ k_mean,
                                                            int8_t* __restrict__ k_codes,
                                                            float* __restrict__ k_scale, int S,
                                                            int nkb) {
   const int bh = blockIdx.x / nkb, blk = blockIdx.x - bh * nkb;
-  quant_block<D, 64, true>(k, k_mean, k_codes, k_scale + (size_t)bh * nkb + blk, S, bh, blk);
+  quant_block<D, 64, true>(k, ks, H, k_mean, k_codes, k_scale + (size_t)bh * nkb + blk, S, bh, blk);
 }
 
 }  // namespace
@@ -222,30 +228,33 @@ int kmean_chunks(int B, int H, int S) {
 }
 
 template <int D>
-hipError_t launch_prepass_d(const uint16_t* q, const uint16_t* k, float* k_mean, double* partial,
-                            int8_t* q_codes, int8_t* k_codes, float* q_scale, float* k_scale,
-                            int B, int H, int S, hipStream_t stream) {
+hipError_t launch_prepass_d(const uint16_t* q, Strides qs, const uint16_t* k, Strides ks,
+                            float* k_mean, double* partial, int8_t* q_codes, int8_t* k_codes,
+                            float* q_scale, float* k_scale, int B, int H, int S, hipStream_t stream) {
   const int BH = B * H;
   const int nch = kmean_chunks(B, H, S);
   const int rows_per = (S + nch - 1) / nch;
   const int nqb = (S + 127) / 128, nkb = (S + 63) / 64;
   hipLaunchKernelGGL(kmean_partial_quant_q_kernel<D>, dim3((unsigned)((long long)BH * (nch + nqb))),
-                     dim3(kThreads), 0, stream, q, k, partial, q_codes, q_scale, S, BH, nch, rows_per, nqb);
+                     dim3(kThreads), 0, stream, q, qs, k, ks, H, partial, q_codes, q_scale, S, BH,
+                     nch, rows_per, nqb);
   hipLaunchKernelGGL(kmean_final_kernel<D>, dim3((unsigned)BH), dim3(kThreads), 0, stream, partial,
                      k_mean, S, nch);
   hipLaunchKernelGGL(quant_k_kernel<D>, dim3((unsigned)((long long)BH * nkb)), dim3(kThreads), 0,
-                     stream, k, k_mean, k_codes, k_scale, S, nkb);
+                     stream, k, ks, H, k_mean, k_codes, k_scale, S, nkb);
   return hipGetLastError();
 }
 
-hipError_t launch_prepass(const void* q, const void* k, float* k_mean, double* partial,
-                          int8_t* q_codes, int8_t* k_codes, float* q_scale, float* k_scale, int B,
-                          int H, int S, int D, hipStream_t stream) {
+hipError_t launch_prepass(const void* q, Strides qs, const void* k, Strides ks, float* k_mean,
+                          double* partial, int8_t* q_codes, int8_t* k_codes, float* q_scale,
+                          float* k_scale, int B, int H, int S, int D, hipStream_t stream) {
   const auto* qq = static_cast<const uint16_t*>(q);
   const auto* kk = static_cast<const uint16_t*>(k);
   if (D == 64)
-    return launch_prepass_d<64>(qq, kk, k_mean, partial, q_codes, k_codes, q_scale, k_scale, B, H, S, stream);
-  return launch_prepass_d<128>(qq, kk, k_mean, partial, q_codes, k_codes, q_scale, k_scale, B, H, S, stream);
+    return launch_prepass_d<64>(qq, qs, kk, ks, k_mean, partial, q_codes, k_codes, q_scale,
+                                k_scale, B, H, S, stream);
+  return launch_prepass_d<128>(qq, qs, kk, ks, k_mean, partial, q_codes, k_codes, q_scale,
+                               k_scale, B, H, S, stream);
 }
 
 }  // namespace ditattn

@@ -22,9 +22,10 @@
  * Conventions shared by every call:
  *   - Tensor pointers are DEVICE pointers, allocated and owned by the caller.  The library
  *     allocates no memory and keeps no state between calls.
- *   - Every tensor is contiguous, row-major, and 16-byte aligned.
+ *   - Every tensor is 16-byte aligned and, except in the *_ex calls (strided views), contiguous
+ *     and row-major.
  *   - Attention tensors are [B, H, S, D]: batch, head, token, channel (channel fastest).
- *     Q, K, V are bf16 (raw 16-bit patterns); O is fp32.
+ *     Q, K, V are bf16 (raw 16-bit patterns); O is fp32 (the *_ex calls: fp32 or bf16).
  *   - `stream` is a hipStream_t (NULL = the default stream).  Each call only enqueues work on
  *     it and returns; results are valid once the caller synchronises with the stream.
  *   - Return value: DITATTN_OK (0) or a negative status.  Arguments are validated before any
@@ -101,6 +102,43 @@ DITATTN_API size_t attn_int8qk_workspace_offsets(int B, int H, int S, int D, siz
 DITATTN_API int attn_fwd_int8qk(const void* q, const void* k, const void* v, float* o,
                     int B, int H, int S, int D, float scale,
                     void* workspace, size_t workspace_bytes, void* stream);
+
+/* ---- extended attention calls: strided views, bf16 output, per-row log-sum-exp --------------
+ *
+ * Same operations as attn_fwd_bf16 / attn_fwd_int8qk, with three additions that the steps
+ * around the kernel need:
+ *   strides   : 12 int64 element strides, for q, k, v, o in this order, each as (batch, head,
+ *               token); the channel axis must be contiguous.  A contiguous [B, H, S, D] tensor
+ *               is {H*S*D, S*D, D}; a [B, S, H, D] tensor (heads interleaved per token) is
+ *               {S*H*D, D, H*D}.  Every stride >= 0 and a multiple of 16 bytes' worth of
+ *               elements (8 for bf16, 4 for fp32); token strides of q, k, v below 2^24.
+ *   out_dtype : DITATTN_OUT_F32 (o fp32) or DITATTN_OUT_BF16 (o bf16, each value the fp32
+ *               result rounded to nearest even)
+ *   lse       : NULL, or fp32 [B, H, S] contiguous, 4-byte aligned, receiving
+ *               lse[b,h,i] = log sum_j exp(s_ij) with s_ij the scaled score of that call (the
+ *               int8 call: of the quantized scores).  Partial results over disjoint key sets
+ *               merge through it: lse = log(e^lse_A + e^lse_B), o = e^(lse_A-lse) o_A +
+ *               e^(lse_B-lse) o_B — how a sequence split over devices (the ring dimension of
+ *               the context-parallel mesh, "ParaAttention" page, Context Parallelism section)
+ *               combines partial outputs.
+ * o and lse must not overlap q, k, v or each other, and o's strides must not map two rows to
+ * one address (identical pointers are rejected; other overlaps are the caller's to avoid).
+ * Errors as the plain calls, plus
+ * DITATTN_EINVAL for a NULL strides array, a bad out_dtype, or a stride that breaks the
+ * rules above. */
+#define DITATTN_OUT_F32 0
+#define DITATTN_OUT_BF16 1
+
+DITATTN_API int attn_fwd_bf16_ex(const void* q, const void* k, const void* v, void* o,
+                                 int out_dtype, float* lse, const int64_t* strides,
+                                 int B, int H, int S, int D, float scale, void* stream);
+
+/* As attn_fwd_int8qk with the additions above; the workspace (size and layout) is the same,
+ * its codes stay contiguous [B, H, S, D] whatever the strides of q and k. */
+DITATTN_API int attn_fwd_int8qk_ex(const void* q, const void* k, const void* v, void* o,
+                                   int out_dtype, float* lse, const int64_t* strides,
+                                   int B, int H, int S, int D, float scale,
+                                   void* workspace, size_t workspace_bytes, void* stream);
 
 /* Workspace of resid_rel_l1, in bytes, for n elements (0 if n < 1). */
 DITATTN_API size_t resid_rel_l1_workspace_bytes(int64_t n);

@@ -30,9 +30,10 @@ def declared_functions():
 
 def test_header_declares_the_three_calls():
     names = declared_functions()
-    for n in ("attn_fwd_bf16", "attn_fwd_int8qk", "resid_rel_l1"):
+    for n in ("attn_fwd_bf16", "attn_fwd_int8qk", "resid_rel_l1", "attn_fwd_bf16_ex",
+              "attn_fwd_int8qk_ex"):
         assert n in names
-    assert len(names) == 7
+    assert len(names) == 9
 
 
 def test_library_exports_every_declared_symbol(L):
@@ -104,6 +105,57 @@ def test_int8_argument_errors(L):
     assert L.attn_fwd_int8qk(*bad, FAKE + 0x8000, need, None) == EINVAL
 
 
+def _contig(H, S, D):
+    return [H * S * D, S * D, D] * 4
+
+
+def _ex(L, strides=None, out_dtype=0, lse=None, q=FAKE, o=FAKE + 0x3000, B=1, H=2, S=64, D=64,
+        int8=False):
+    st = _contig(H, S, D) if strides is None else strides
+    arr = (ctypes.c_int64 * 12)(*st) if st is not False else None
+    args = [q, FAKE + 0x1000, FAKE + 0x2000, o, out_dtype, lse, arr, B, H, S, D, 0.125]
+    if int8:
+        need = L.attn_int8qk_workspace_bytes(B, H, S, D)
+        return L.attn_fwd_int8qk_ex(*args, FAKE + 0x8000, need - 1, None)
+    return L.attn_fwd_bf16_ex(*args, None)
+
+
+@pytest.mark.parametrize("int8", [False, True])
+def test_ex_argument_errors(L, int8):
+    # every bad call fails validation before anything is launched; the int8 calls get a too
+    # small workspace, so a call that passed validation would return EWORKSPACE, not launch
+    ok = EWS if int8 else None
+    assert _ex(L, strides=False, int8=int8) == EINVAL                     # NULL strides
+    for bad in (-1, 2, 7):
+        assert _ex(L, out_dtype=bad, int8=int8) == EINVAL
+    assert _ex(L, q=None, int8=int8) == EINVAL
+    assert _ex(L, o=FAKE, int8=int8) == EINVAL                           # o aliases q
+    assert _ex(L, q=FAKE + 8, int8=int8) == EINVAL                       # misaligned
+    assert _ex(L, lse=FAKE + 0x3000, int8=int8) == EINVAL                # lse aliases o
+    assert _ex(L, lse=FAKE + 0x4002, int8=int8) == EINVAL                # lse misaligned
+    assert _ex(L, D=96, strides=_contig(2, 64, 96), int8=int8) == EUNSUP
+    for t in range(4):
+        for a in range(3):
+            st = _contig(2, 64, 64); st[3 * t + a] = -64
+            assert _ex(L, strides=st, int8=int8) == EINVAL               # negative stride
+            st = _contig(2, 64, 64); st[3 * t + a] += 2
+            assert _ex(L, strides=st, int8=int8) == EINVAL               # not 16-byte steps
+    for t in range(3):
+        st = _contig(2, 64, 64); st[3 * t + 2] = 1 << 24
+        assert _ex(L, strides=st, int8=int8) == EINVAL                   # token stride too big
+    # fp32 output: strides in steps of 4 elements pass validation; bf16 output needs 8
+    st = _contig(2, 64, 64); st[11] = 68
+    if int8:
+        assert _ex(L, strides=st, int8=True) == ok
+        assert _ex(L, strides=st, out_dtype=1, int8=True) == EINVAL
+        # the output's token stride has no 2^24 limit; stride 0 (broadcast inputs) is valid
+        st = _contig(2, 64, 64); st[11] = 1 << 30; st[0] = st[1] = 0
+        assert _ex(L, strides=st, int8=True) == ok
+        assert _ex(L, lse=FAKE + 0x4004, int8=True) == ok
+    else:
+        assert _ex(L, strides=st, out_dtype=1) == EINVAL
+
+
 def test_rel_l1_argument_errors(L):
     need = L.resid_rel_l1_workspace_bytes(100)
     assert L.resid_rel_l1(None, FAKE, 100, FAKE + 0x1000, FAKE + 0x2000, need, None) == EINVAL
@@ -120,4 +172,21 @@ def test_binding_rejects_cpu_tensors():
     with pytest.raises(ValueError):
         dta.attn_fwd_bf16(x, x, x)
     with pytest.raises(ValueError):
+        dta.attn_fwd_bf16(x, x, x, out_dtype=torch.bfloat16, lse=True)
+    with pytest.raises(ValueError):
+        dta.attn_fwd_int8qk(x, x, x, lse=True)
+    with pytest.raises(ValueError):
         dta.resid_rel_l1(x, x)
+
+
+def test_binding_strides_of_views():
+    """The (batch, head, token) strides the binding hands to the extended calls."""
+    import torch
+    import diffusion_transformer_attention_amd as dta
+    B, S, H, D = 2, 40, 3, 64
+    bshd = torch.zeros(B, S, H, D, dtype=torch.bfloat16).transpose(1, 2)
+    assert dta._bhs_strides(bshd) == [S * H * D, D, H * D]
+    qkv = torch.zeros(B, S, 3, H, D, dtype=torch.bfloat16)        # fused QKV projection
+    assert dta._bhs_strides(qkv[:, :, 1].transpose(1, 2)) == [S * 3 * H * D, D, 3 * H * D]
+    one = torch.zeros(1, 1, S, D, dtype=torch.bfloat16)
+    assert dta._bhs_strides(one) == [0, 0, D]                     # size-1 axes never stepped
