@@ -141,6 +141,32 @@ def time_image_shape(torch, dta, stream, ev, iters=50):
     return out
 
 
+def time_fbcache(torch, dta, stream, ev, a, b, iters=20):
+    """First Block Cache calls on the residual pair: the decision (a rel-L1 pass plus the
+    decision, 4 bytes per element) and the residual add (6 bytes per element), GB/s."""
+    out_h = torch.empty_like(a)
+    st = dta.fbcache_state("cuda")
+    cfg = dta.FBCacheConfig()
+    ws = torch.empty(dta.rel_l1_workspace_bytes(a.numel()), dtype=torch.uint8, device="cuda")
+    res = {}
+    for name, fn, nbytes in (
+            ("decide", lambda: dta.fbcache_decide(a, b, st, cfg, workspace=ws), 4.0 * a.numel()),
+            ("resid_add", lambda: dta.resid_add(a, b, out=out_h), 6.0 * a.numel())):
+        for _ in range(3):
+            fn()
+        e0, e1 = ev(), ev()
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(iters):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / iters
+        gbs = nbytes / (ms * 1e-3) / 1e9
+        res[name] = {"ms": ms, "gbs": gbs, "frac_hbm_peak": gbs / PEAK_HBM_GBS}
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -148,7 +174,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--headline-only", action="store_true",
-                    help="skip the extra S=4608 timing (profiling runs: one shape per kernel)")
+                    help="skip the extra timings (S=4608 attention, First Block Cache calls): "
+                         "profiling runs, one shape per kernel")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy three times (the "
                          "reference kernel for scaling HBM byte counters) and exit")
@@ -232,6 +259,7 @@ def main():
 
     # image-DiT shape, timed separately (not part of `value`)
     img = None if args.headline_only else time_image_shape(torch, dta, stream, ev)
+    fbc = None if args.headline_only else time_fbcache(torch, dta, stream, ev, a, b)
 
     traffic = load_traffic()
     line = {
@@ -260,6 +288,7 @@ def main():
                        "note": "whole call: K mean + quantization + attention"},
             "rel_l1": {"ms": ms_rl1, "gbs": rl1_gbs, "frac_hbm_peak": rl1_gbs / PEAK_HBM_GBS},
             "image_S4608": img,
+            "fbcache_118800x3072": fbc,
             "wall_s_timed": wall,
         },
     }

@@ -31,6 +31,7 @@ from __future__ import annotations
 import numpy as np
 
 TAG_Q, TAG_K, TAG_V, TAG_KOFF, TAG_RL1_B, TAG_RL1_NOISE = 0, 1, 2, 3, 4, 5
+TAG_FB_H0, TAG_FB_STEP, TAG_FB_FIRST, TAG_FB_REST = 6, 7, 8, 9
 
 # name -> (workload_id, B, H, S, D, K-offset variance)
 WORKLOADS = {
@@ -121,6 +122,32 @@ def residual_pair(rows: int, cols: int = RL1_HIDDEN, workload_id: int = 4, noise
     n = _stream(workload_id, TAG_RL1_NOISE).standard_normal((rows, cols))
     a = f64_to_bf16_bits(bf16_to_f64(b) + noise * n)
     return a, b
+
+
+def hidden_state_steps(steps: int, rows: int, cols: int = RL1_HIDDEN, drift=None,
+                       workload_id: int = 5):
+    """Synthetic hidden states of a denoising run, as bf16 bits [rows, cols] per step:
+    h0 (the step's input), h1 (after the first block) and hN (after the last block).
+
+    h0 and the first block's own contribution (0.5 * N(0, 1) at step 0) are random walks over
+    the steps: step t moves each by drift[t] * N(0, 1).  The remaining blocks add a fresh
+    N(0, 1).  Small drift makes consecutive first-block residuals close, and the distance to
+    an older step grows with the number of steps in between."""
+    drift = [0.02] * steps if drift is None else list(drift)
+    g0 = _stream(workload_id, TAG_FB_H0)
+    first = 0.5 * _stream(workload_id, TAG_FB_FIRST).standard_normal((rows, cols))
+    h = g0.standard_normal((rows, cols))
+    out = []
+    for t in range(steps):
+        gs = _stream(workload_id, TAG_FB_STEP, t)
+        h = h + drift[t] * gs.standard_normal((rows, cols))
+        first = first + drift[t] * gs.standard_normal((rows, cols))
+        rest = _stream(workload_id, TAG_FB_REST, t).standard_normal((rows, cols))
+        h0 = f64_to_bf16_bits(h)
+        h1 = f64_to_bf16_bits(bf16_to_f64(h0) + first)
+        hn = f64_to_bf16_bits(bf16_to_f64(h1) + rest)
+        out.append((h0, h1, hn))
+    return out
 
 
 def sample_rows(S: int, n_random: int, seed: int, edge: int = 64) -> np.ndarray:

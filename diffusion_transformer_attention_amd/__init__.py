@@ -11,8 +11,11 @@ Entry points (same names as the C ABI in include/ditattn.h):
   attn_fwd_bf16(q, k, v, out=None, scale=None) -> out
   attn_fwd_int8qk(q, k, v, out=None, scale=None, workspace=None) -> out
   resid_rel_l1(a, b, out=None, workspace=None) -> out (fp32 device scalar, shape [1])
+  fbcache_decide(resid, prev_resid, state, config, workspace=None) -> state
+  resid_add(a, b, out=None) -> out;  resid_sub(a, b, out=None) -> out
 
-plus helpers for the int8 workspace (int8qk_workspace, int8qk_views) and the library path.
+plus helpers for the int8 workspace (int8qk_workspace, int8qk_views), the First Block Cache
+state (FBCacheConfig, fbcache_state, fbcache_state_values) and the library path.
 
 The attention calls also take strided [B, H, S, D] views (channel axis contiguous), for
 instance q.transpose(1, 2) of a [B, S, H, D] tensor or a slice of a fused QKV projection, an
@@ -29,8 +32,9 @@ import os
 import torch  # loaded first: the library then binds to the HIP runtime torch already holds
 
 __all__ = ["attn_fwd_bf16", "attn_fwd_int8qk", "resid_rel_l1", "int8qk_workspace",
-           "int8qk_views", "int8qk_workspace_bytes", "rel_l1_workspace_bytes", "lib",
-           "LIB_PATH", "DitAttnError"]
+           "int8qk_views", "int8qk_workspace_bytes", "rel_l1_workspace_bytes", "fbcache_decide",
+           "resid_add", "resid_sub", "FBCacheConfig", "fbcache_state", "fbcache_state_values",
+           "lib", "LIB_PATH", "DitAttnError"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libditattn.so")
 
@@ -38,6 +42,17 @@ STATUS = {0: "DITATTN_OK", -1: "DITATTN_EINVAL", -2: "DITATTN_EUNSUPPORTED",
           -3: "DITATTN_EWORKSPACE", -4: "DITATTN_EHIP"}
 
 _lib = None
+
+
+class FBCacheConfig(ctypes.Structure):
+    """ditattn_fbcache_config: the cache policy (defaults: the DBCache defaults)."""
+    _fields_ = [("residual_diff_threshold", ctypes.c_float), ("max_warmup_steps", ctypes.c_int32),
+                ("max_cached_steps", ctypes.c_int32), ("max_continuous_cached_steps", ctypes.c_int32)]
+
+    def __init__(self, residual_diff_threshold=0.24, max_warmup_steps=4, max_cached_steps=-1,
+                 max_continuous_cached_steps=3):
+        super().__init__(residual_diff_threshold, max_warmup_steps, max_cached_steps,
+                         max_continuous_cached_steps)
 
 
 class DitAttnError(RuntimeError):
@@ -73,6 +88,12 @@ def lib() -> ctypes.CDLL:
     L.resid_rel_l1_workspace_bytes.restype = sz
     L.resid_rel_l1.argtypes = [vp, vp, i64, vp, vp, sz, vp]
     L.resid_rel_l1.restype = i
+    L.fbcache_decide.argtypes = [vp, vp, i64, ctypes.POINTER(FBCacheConfig), vp, vp, sz, vp]
+    L.fbcache_decide.restype = i
+    L.resid_add.argtypes = [vp, vp, vp, i64, vp]
+    L.resid_add.restype = i
+    L.resid_sub.argtypes = [vp, vp, vp, i64, vp]
+    L.resid_sub.restype = i
     L.ditattn_status_string.argtypes = [i]
     L.ditattn_status_string.restype = ctypes.c_char_p
     _lib = L
@@ -236,3 +257,67 @@ def resid_rel_l1(a, b, out=None, workspace=None):
     _check(lib().resid_rel_l1(_ptr(a), _ptr(b), n, _ptr(out), _ptr(workspace), workspace.numel(),
                               _stream(a)))
     return out
+
+
+# ---- First Block Cache ----------------------------------------------------------------------
+
+def fbcache_state(device) -> torch.Tensor:
+    """A zeroed ditattn_fbcache_state (32 bytes of device memory) for a new run."""
+    return torch.zeros(8, dtype=torch.int32, device=device)
+
+
+def fbcache_state_values(state: torch.Tensor) -> dict:
+    """The state's fields, read back to the host (synchronises with the state's stream)."""
+    h = state.cpu()
+    return {"steps": int(h[0]), "cached_steps": int(h[1]), "continuous_cached_steps": int(h[2]),
+            "use_cache": int(h[3]), "diff": float(h[4:5].view(torch.float32)[0])}
+
+
+def _bf16_flat(name, t):
+    if not t.is_cuda or t.dtype != torch.bfloat16 or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous bf16 CUDA tensor")
+
+
+def fbcache_decide(resid, prev_resid, state, config=None, workspace=None):
+    """One step's cache decision on `state` (from fbcache_state); prev_resid None = no reference.
+    The decision stays on the device: state[3] (1 = reuse the cache)."""
+    _bf16_flat("resid", resid)
+    if prev_resid is not None:
+        _bf16_flat("prev_resid", prev_resid)
+        if prev_resid.shape != resid.shape:
+            raise ValueError("resid and prev_resid must have the same shape")
+    if state.dtype != torch.int32 or state.numel() != 8 or not state.is_cuda or not state.is_contiguous():
+        raise ValueError("state must come from fbcache_state()")
+    cfg = FBCacheConfig() if config is None else config
+    n = resid.numel()
+    if prev_resid is not None and workspace is None:
+        workspace = torch.empty(max(rel_l1_workspace_bytes(n), 1), dtype=torch.uint8, device=resid.device)
+    ws_n = workspace.numel() if workspace is not None else 0
+    _check(lib().fbcache_decide(_ptr(resid), _ptr(prev_resid), n, ctypes.byref(cfg), _ptr(state),
+                                _ptr(workspace), ws_n, _stream(resid)))
+    return state
+
+
+def _resid_op(fn, a, b, out):
+    _bf16_flat("a", a)
+    _bf16_flat("b", b)
+    if a.shape != b.shape:
+        raise ValueError("a and b must have the same shape")
+    if out is None:
+        out = torch.empty_like(a)
+    else:
+        _bf16_flat("out", out)
+        if out.shape != a.shape:
+            raise ValueError("out must have the shape of a")
+    _check(fn(_ptr(a), _ptr(b), _ptr(out), a.numel(), _stream(a)))
+    return out
+
+
+def resid_add(a, b, out=None):
+    """out = a + b over bf16 tensors, each value rounded once (out may be a or b)."""
+    return _resid_op(lib().resid_add, a, b, out)
+
+
+def resid_sub(a, b, out=None):
+    """out = a - b over bf16 tensors, each value rounded once (out may be a or b)."""
+    return _resid_op(lib().resid_sub, a, b, out)

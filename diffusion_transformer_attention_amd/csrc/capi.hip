@@ -111,6 +111,20 @@ int int8qk_run(const ditattn::AttnCall& ac, void* workspace, size_t workspace_by
   return status_of(ditattn::launch_attn_int8(ac, q_codes, k_codes, q_scale, k_scale, s));
 }
 
+// Elementwise bf16 calls: out may be a or b exactly, but must not partly overlap either.
+int check_elementwise(const void* a, const void* b, const void* out, int64_t n) {
+  if (!a || !b || !out || n < 1) return DITATTN_EINVAL;
+  if (!aligned(a, 16) || !aligned(b, 16) || !aligned(out, 16)) return DITATTN_EINVAL;
+  if (n > (INT64_MAX / 2)) return DITATTN_EINVAL;
+  const uintptr_t bytes = (uintptr_t)n * 2;
+  auto partly = [&](const void* x) {
+    const uintptr_t p = reinterpret_cast<uintptr_t>(out), q = reinterpret_cast<uintptr_t>(x);
+    return p != q && p < q + bytes && q < p + bytes;
+  };
+  if (partly(a) || partly(b)) return DITATTN_EINVAL;
+  return DITATTN_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -203,6 +217,36 @@ int resid_rel_l1(const void* a, const void* b, int64_t n, float* out, void* work
     return DITATTN_EWORKSPACE;
   return status_of(ditattn::launch_rel_l1(a, b, n, out, static_cast<double*>(workspace),
                                           static_cast<hipStream_t>(stream)));
+}
+
+int fbcache_decide(const void* resid, const void* prev_resid, int64_t n,
+                   const ditattn_fbcache_config* cfg, ditattn_fbcache_state* state,
+                   void* workspace, size_t workspace_bytes, void* stream) {
+  if (!resid || !cfg || !state || n < 1) return DITATTN_EINVAL;
+  if (!aligned(resid, 16) || !aligned(state, 4)) return DITATTN_EINVAL;
+  if (prev_resid && !aligned(prev_resid, 16)) return DITATTN_EINVAL;
+  const ditattn_fbcache_config c = *cfg;
+  if (!isfinite(c.residual_diff_threshold) || c.residual_diff_threshold < 0.f) return DITATTN_EINVAL;
+  if (c.max_warmup_steps < 0 || c.max_cached_steps < -1 || c.max_continuous_cached_steps < -1)
+    return DITATTN_EINVAL;
+  if (prev_resid && (!workspace || !aligned(workspace, 8) ||
+                     workspace_bytes < resid_rel_l1_workspace_bytes(n)))
+    return DITATTN_EWORKSPACE;
+  return status_of(ditattn::launch_fbcache_decide(resid, prev_resid, n, c, state,
+                                                  static_cast<double*>(workspace),
+                                                  static_cast<hipStream_t>(stream)));
+}
+
+int resid_add(const void* a, const void* b, void* out, int64_t n, void* stream) {
+  const int st = check_elementwise(a, b, out, n);
+  if (st != DITATTN_OK) return st;
+  return status_of(ditattn::launch_resid_addsub(a, b, out, n, false, static_cast<hipStream_t>(stream)));
+}
+
+int resid_sub(const void* a, const void* b, void* out, int64_t n, void* stream) {
+  const int st = check_elementwise(a, b, out, n);
+  if (st != DITATTN_OK) return st;
+  return status_of(ditattn::launch_resid_addsub(a, b, out, n, true, static_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"

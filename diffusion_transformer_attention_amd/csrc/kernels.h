@@ -7,6 +7,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include "ditattn.h"
+
 namespace ditattn {
 
 // Element strides of a [B, H, S, D] tensor view: batch, head, token.  The channel axis is
@@ -50,5 +52,15 @@ int rel_l1_blocks(int64_t n);
 
 hipError_t launch_rel_l1(const void* a, const void* b, int64_t n, float* out, double* partial,
                          hipStream_t stream);
+
+// The relative-L1 pass of resid against prev_resid (skipped when prev_resid is null) followed by
+// one First Block Cache decision on *state (device memory).  partial: rel_l1_blocks(n) pairs.
+hipError_t launch_fbcache_decide(const void* resid, const void* prev_resid, int64_t n,
+                                 const ditattn_fbcache_config& cfg, ditattn_fbcache_state* state,
+                                 double* partial, hipStream_t stream);
+
+// out = bf16(a + b) (SUB: a - b) elementwise over n bf16 values, each rounded once.
+hipError_t launch_resid_addsub(const void* a, const void* b, void* out, int64_t n, bool sub,
+                               hipStream_t stream);
 
 }  // namespace ditattn

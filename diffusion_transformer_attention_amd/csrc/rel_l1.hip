@@ -7,6 +7,11 @@
 // contiguous range with 16-byte nontemporal loads, eight iterations (256 bytes per thread) in
 // flight, fp32 per-thread sums, an fp64 reduction per workgroup, and a one-workgroup fp64
 // finish in a fixed order (no atomics, so the result is deterministic).
+//
+// fbcache_decide runs the same pass and then, in the finishing workgroup, the cache decision
+// of the step: reuse only past the warmup steps, with a difference below the threshold, and
+// within the caps on cached and consecutively cached steps (DBCache parameters of the
+// "Cache-DiT acceleration" page).  The decision and the counters stay in device memory.
 #include "device_common.h"
 #include "kernels.h"
 
@@ -104,6 +109,44 @@ __global__ __launch_bounds__(kThreads) void rel_l1_final_kernel(const double* __
   }
 }
 
+// The same finish, followed by one First Block Cache decision on the state in device memory
+// (thread 0 reads, decides and writes it back; calls on one state are ordered by the stream).
+// nblocks == 0: there is no previous residual, so no difference and the step computes.
+__global__ __launch_bounds__(kThreads) void fbcache_final_kernel(const double* __restrict__ partial,
+                                                                 int nblocks,
+                                                                 ditattn_fbcache_config cfg,
+                                                                 ditattn_fbcache_state* state) {
+  double x = 0.0, y = 0.0;
+  for (int j = threadIdx.x; j < nblocks; j += kThreads) {
+    x += partial[2 * j];
+    y += partial[2 * j + 1];
+  }
+  block_reduce2(x, y);
+  if (threadIdx.x == 0) {
+    const bool has_prev = nblocks > 0;
+    float r = __builtin_nanf("");
+    if (has_prev) {
+      if (y == 0.0)
+        r = (x == 0.0) ? 0.f : INFINITY;
+      else
+        r = (float)(x / y);
+    }
+    ditattn_fbcache_state st = *state;
+    // warmup, a difference below the threshold (false for NaN), and both caps
+    bool use = st.steps >= cfg.max_warmup_steps && has_prev && r < cfg.residual_diff_threshold;
+    if (cfg.max_cached_steps >= 0 && st.cached_steps >= cfg.max_cached_steps) use = false;
+    if (cfg.max_continuous_cached_steps >= 0 &&
+        st.continuous_cached_steps >= cfg.max_continuous_cached_steps)
+      use = false;
+    st.steps += 1;
+    st.cached_steps += use ? 1 : 0;
+    st.continuous_cached_steps = use ? st.continuous_cached_steps + 1 : 0;
+    st.use_cache = use ? 1 : 0;
+    st.diff = r;
+    *state = st;
+  }
+}
+
 }  // namespace
 
 int rel_l1_blocks(int64_t n) {
@@ -120,6 +163,21 @@ hipError_t launch_rel_l1(const void* a, const void* b, int64_t n, float* out, do
   hipLaunchKernelGGL(rel_l1_partial_kernel, dim3(nb), dim3(kThreads), 0, stream,
                      static_cast<const uint16_t*>(a), static_cast<const uint16_t*>(b), n, partial);
   hipLaunchKernelGGL(rel_l1_final_kernel, dim3(1), dim3(kThreads), 0, stream, partial, nb, out);
+  return hipGetLastError();
+}
+
+hipError_t launch_fbcache_decide(const void* resid, const void* prev_resid, int64_t n,
+                                 const ditattn_fbcache_config& cfg, ditattn_fbcache_state* state,
+                                 double* partial, hipStream_t stream) {
+  int nb = 0;
+  if (prev_resid != nullptr) {
+    nb = rel_l1_blocks(n);
+    hipLaunchKernelGGL(rel_l1_partial_kernel, dim3(nb), dim3(kThreads), 0, stream,
+                       static_cast<const uint16_t*>(resid), static_cast<const uint16_t*>(prev_resid),
+                       n, partial);
+  }
+  hipLaunchKernelGGL(fbcache_final_kernel, dim3(1), dim3(kThreads), 0, stream, partial, nb, cfg,
+                     state);
   return hipGetLastError();
 }
 

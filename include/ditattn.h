@@ -1,7 +1,8 @@
 /*
  * ditattn.h -- C ABI of the DiT attention library for AMD Instinct MI355X (gfx950).
  *
- * Three operations, all non-causal and all on one GPU:
+ * Three operations, all non-causal and all on one GPU (and, further below, the extended
+ * attention calls and the First Block Cache step built around resid_rel_l1):
  *
  *   attn_fwd_bf16    O = softmax(Q K^T * scale) V per (batch, head), QK^T and PV on bf16
  *                    matrix cores.  The DiT self-attention that the "Diffusion Attention
@@ -153,6 +154,62 @@ DITATTN_API size_t resid_rel_l1_workspace_bytes(int64_t n);
  * deterministic for a given n. */
 DITATTN_API int resid_rel_l1(const void* a, const void* b, int64_t n, float* out,
                  void* workspace, size_t workspace_bytes, void* stream);
+
+/* ---- First Block Cache ------------------------------------------------------------------
+ *
+ * A denoising step of a DiT may skip its remaining transformer blocks when the residual its
+ * first block adds differs little from the one it added at the latest computed step; it then
+ * reuses the residual the remaining blocks added at that step ("ParaAttention" page, First
+ * Block Cache section; parameters as the DBCache parameters of the "Cache-DiT acceleration"
+ * page, vLLM-Omni user guide).  Per step, on the caller's stream:
+ *   r1 = resid_sub(h1, h0)                       h0: step input, h1: first block's output
+ *   fbcache_decide(r1, r1_ref, ...)              r1_ref: r1 of the latest computed step
+ *   use_cache (state, device) == 1:  out = resid_add(h1, rest)           -- skip the blocks
+ *                           == 0:  hN = remaining blocks(h1); rest = resid_sub(hN, h1);
+ *                                  r1_ref = r1 (swap two residual buffers, no copy)
+ * The caller reads the 4-byte decision from device memory to branch (one synchronisation). */
+
+/* Cache policy (host memory, read at each call). */
+typedef struct ditattn_fbcache_config {
+  float residual_diff_threshold;       /* reuse only when the difference is below this (fp32) */
+  int32_t max_warmup_steps;            /* steps 0 .. max_warmup_steps-1 always compute (>= 0) */
+  int32_t max_cached_steps;            /* at most this many cached steps in the run; -1: no cap */
+  int32_t max_continuous_cached_steps; /* at most this many cached steps in a row; -1: no cap */
+} ditattn_fbcache_config;
+
+/* Per-run state, in DEVICE memory (32 bytes, 4-byte aligned, caller owned).  All zero before
+ * the first step of a run; each fbcache_decide call advances it by one step. */
+typedef struct ditattn_fbcache_state {
+  int32_t steps;                    /* steps decided so far */
+  int32_t cached_steps;             /* of them, served from the cache */
+  int32_t continuous_cached_steps;  /* cached steps since the latest computed step */
+  int32_t use_cache;                /* decision of the latest step: 1 reuse, 0 compute */
+  float diff;                       /* that step's difference (NaN: no reference residual) */
+  int32_t reserved[3];
+} ditattn_fbcache_state;
+
+/* One step's cache decision.
+ *   resid       : bf16 device array of n elements, this step's first-block residual
+ *   prev_resid  : the reference residual (bf16, n elements), or NULL when there is none yet
+ *                 (the step then computes)
+ *   n           : >= 1
+ *   cfg         : host pointer; threshold finite and >= 0, warmup >= 0, caps >= -1
+ *   state       : device pointer to the run's ditattn_fbcache_state
+ *   workspace   : device buffer of >= resid_rel_l1_workspace_bytes(n) bytes (may be NULL when
+ *                 prev_resid is NULL)
+ * The difference is resid_rel_l1(resid, prev_resid) (same kernel, same value).  The step
+ * reuses the cache iff steps >= max_warmup_steps, a reference exists, diff < threshold (false
+ * for NaN), cached_steps < max_cached_steps (or no cap) and continuous_cached_steps <
+ * max_continuous_cached_steps (or no cap).  Calls on one state must be ordered (one stream). */
+DITATTN_API int fbcache_decide(const void* resid, const void* prev_resid, int64_t n,
+                               const ditattn_fbcache_config* cfg, ditattn_fbcache_state* state,
+                               void* workspace, size_t workspace_bytes, void* stream);
+
+/* out = a + b and out = a - b over n bf16 values (device arrays, 16-byte aligned, n >= 1),
+ * each result the exact value rounded once to bf16 (nearest, ties to even).  out may be a or b
+ * itself; any other overlap is rejected (DITATTN_EINVAL). */
+DITATTN_API int resid_add(const void* a, const void* b, void* out, int64_t n, void* stream);
+DITATTN_API int resid_sub(const void* a, const void* b, void* out, int64_t n, void* stream);
 
 /* Static English description of a status code (never NULL). */
 DITATTN_API const char* ditattn_status_string(int status);

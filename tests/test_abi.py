@@ -31,9 +31,9 @@ def declared_functions():
 def test_header_declares_the_three_calls():
     names = declared_functions()
     for n in ("attn_fwd_bf16", "attn_fwd_int8qk", "resid_rel_l1", "attn_fwd_bf16_ex",
-              "attn_fwd_int8qk_ex"):
+              "attn_fwd_int8qk_ex", "fbcache_decide", "resid_add", "resid_sub"):
         assert n in names
-    assert len(names) == 9
+    assert len(names) == 12
 
 
 def test_library_exports_every_declared_symbol(L):
@@ -165,6 +165,58 @@ def test_rel_l1_argument_errors(L):
     assert L.resid_rel_l1(FAKE, FAKE + 0x100, 100, FAKE + 0x1000, FAKE + 0x2000, need - 1, None) == EWS
 
 
+def test_fbcache_struct_layout_matches_header():
+    import diffusion_transformer_attention_amd as dta
+    assert ctypes.sizeof(dta.FBCacheConfig) == 16
+    cfg = dta.FBCacheConfig()
+    assert (round(cfg.residual_diff_threshold, 6), cfg.max_warmup_steps, cfg.max_cached_steps,
+            cfg.max_continuous_cached_steps) == (0.24, 4, -1, 3)
+    text = open(HEADER).read()
+    body = text[text.index("typedef struct ditattn_fbcache_state"):]
+    body = body[:body.index("} ditattn_fbcache_state;")]
+    # 4 int32 + 1 float + 3 reserved int32 = 32 bytes, the size fbcache_state() allocates
+    assert body.count("int32_t") == 5 and "reserved[3]" in body and body.count("float") == 1
+
+
+def test_fbcache_argument_errors(L):
+    import diffusion_transformer_attention_amd as dta
+    need = L.resid_rel_l1_workspace_bytes(100)
+    R, P, ST, WS = FAKE, FAKE + 0x1000, FAKE + 0x2000, FAKE + 0x3000
+
+    def call(cfg=None, resid=R, prev=P, n=100, state=ST, ws=WS, ws_bytes=need):
+        c = dta.FBCacheConfig() if cfg is None else cfg
+        return L.fbcache_decide(resid, prev, n, ctypes.byref(c), state, ws, ws_bytes, None)
+
+    assert L.fbcache_decide(R, P, 100, None, ST, WS, need, None) == EINVAL   # no config
+    assert call(resid=None) == EINVAL
+    assert call(state=None) == EINVAL
+    assert call(n=0) == EINVAL
+    assert call(resid=R + 8) == EINVAL
+    assert call(prev=P + 8) == EINVAL
+    assert call(state=ST + 2) == EINVAL
+    for bad in (dta.FBCacheConfig(residual_diff_threshold=-0.1),
+                dta.FBCacheConfig(residual_diff_threshold=float("nan")),
+                dta.FBCacheConfig(residual_diff_threshold=float("inf")),
+                dta.FBCacheConfig(max_warmup_steps=-1),
+                dta.FBCacheConfig(max_cached_steps=-2),
+                dta.FBCacheConfig(max_continuous_cached_steps=-2)):
+        assert call(cfg=bad) == EINVAL
+    assert call(ws=None) == EWS
+    assert call(ws_bytes=need - 1) == EWS
+
+
+def test_resid_addsub_argument_errors(L):
+    A, B, O = FAKE, FAKE + 0x1000, FAKE + 0x2000
+    for fn in (L.resid_add, L.resid_sub):
+        assert fn(None, B, O, 64, None) == EINVAL
+        assert fn(A, B, None, 64, None) == EINVAL
+        assert fn(A, B, O, 0, None) == EINVAL
+        assert fn(A + 2, B, O, 64, None) == EINVAL
+        assert fn(A, B, O + 8, 64, None) == EINVAL
+        assert fn(A, B, A + 16, 64, None) == EINVAL      # out overlaps a partly
+        assert fn(A, B, B - 16, 64, None) == EINVAL      # out overlaps b partly
+
+
 def test_binding_rejects_cpu_tensors():
     import torch
     import diffusion_transformer_attention_amd as dta
@@ -177,6 +229,10 @@ def test_binding_rejects_cpu_tensors():
         dta.attn_fwd_int8qk(x, x, x, lse=True)
     with pytest.raises(ValueError):
         dta.resid_rel_l1(x, x)
+    with pytest.raises(ValueError):
+        dta.resid_add(x, x)
+    with pytest.raises(ValueError):
+        dta.fbcache_decide(x, None, torch.zeros(8, dtype=torch.int32))
 
 
 def test_binding_strides_of_views():
