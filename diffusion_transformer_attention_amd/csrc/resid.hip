@@ -4,9 +4,10 @@
 // output is the first block's output plus the residual the remaining blocks added at the latest
 // computed step; when it computes, that residual is formed as the final hidden states minus
 // the first block's output.  Both are elementwise over the hidden states, bound by HBM
-// bandwidth (6 bytes per element: two bf16 reads, one bf16 write).  Each workgroup streams one
-// contiguous range of 16-byte chunks, four chunks per thread in flight, with nontemporal loads
-// and stores (nothing is reread).  The sum is formed in fp32 and rounded once to bf16 (nearest
+// bandwidth (6 bytes per element: two bf16 reads, one bf16 write).  A grid-stride loop over
+// groups of 16-byte chunks, four per thread in flight, with nontemporal loads and stores
+// (nothing is reread); at [118800, 3072] each workgroup takes one group (measured 6.4 TB/s
+// against 5.0 for one contiguous range per workgroup).  The sum is formed in fp32 and rounded once to bf16 (nearest
 // even); the fp32 rounding before it cannot change the result (24 >= 2 * 8 + 2 bits), so each
 // value is the exact sum or difference rounded once.
 #include "device_common.h"
@@ -18,7 +19,7 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kUnroll = 4;
-constexpr int kMaxBlocks = 8192;
+constexpr int kMaxBlocks = 65536;
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 
@@ -44,11 +45,11 @@ __global__ __launch_bounds__(kThreads) void resid_addsub_kernel(const uint16_t* 
   const u32x4* a8 = reinterpret_cast<const u32x4*>(a);
   const u32x4* b8 = reinterpret_cast<const u32x4*>(b);
   u32x4* o8 = reinterpret_cast<u32x4*>(out);
-  const int64_t per = (n8 + gridDim.x - 1) / gridDim.x;
-  const int64_t beg = (int64_t)blockIdx.x * per;
-  const int64_t end = beg + per < n8 ? beg + per : n8;
-  int64_t i = beg + threadIdx.x;
-  for (; i + (kUnroll - 1) * kThreads < end; i += kUnroll * kThreads) {
+  // grid-stride over groups of kUnroll * kThreads chunks (one group per workgroup when the
+  // grid is not capped)
+  const int64_t step = (int64_t)gridDim.x * kUnroll * kThreads;
+  int64_t i = (int64_t)blockIdx.x * kUnroll * kThreads + threadIdx.x;
+  for (; i + (kUnroll - 1) * kThreads < n8; i += step) {
     u32x4 va[kUnroll], vb[kUnroll];
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
@@ -59,7 +60,7 @@ __global__ __launch_bounds__(kThreads) void resid_addsub_kernel(const uint16_t* 
     for (int u = 0; u < kUnroll; ++u)
       __builtin_nontemporal_store(addsub8<SUB>(va[u], vb[u]), o8 + i + u * kThreads);
   }
-  for (; i < end; i += kThreads)
+  for (; i < n8; i += kThreads)
     __builtin_nontemporal_store(
         addsub8<SUB>(__builtin_nontemporal_load(a8 + i), __builtin_nontemporal_load(b8 + i)), o8 + i);
 
