@@ -163,3 +163,32 @@ def log_sum_exp_int8(q_codes, q_scale, k_codes, k_scale, scale: float | None = N
                 m = sc.max(axis=1)
                 out[b, h, r0:r0 + 1024] = m + np.log(np.exp(sc - m[:, None]).sum(axis=1))
     return out
+
+
+def probe_rows(S: int, n_rows: int) -> np.ndarray:
+    """The query rows a quantization-error probe samples: row i = floor((2i + 1) S / (2 n_rows)),
+    the midpoint of the i-th of n_rows equal bins of [0, S) (this library's choice)."""
+    i = np.arange(n_rows, dtype=np.int64)
+    return (2 * i + 1) * S // (2 * n_rows)
+
+
+def quant_probe_error(q, k, v, n_rows: int, scale: float | None = None):
+    """Relative L2 error of the int8-QK output against exact attention on the sampled rows.
+
+    The "TMAP image-to-video inference acceleration" page (section on preserving video quality)
+    keeps some attention layers in full precision, chosen by the per-layer error of the
+    quantized attention over the denoising steps; this is that error for one call:
+    sqrt(sum |o_int8 - o|^2 / sum |o|^2) over the rows probe_rows(S, n_rows) of every (b, h)
+    (o = exact attention, o_int8 = attention_int8 on this module's quantization), overall and
+    per (b, h).  q, k, v: fp64 [B, H, S, D] holding bf16 values.  Returns (overall, [B, H])."""
+    q = np.asarray(q, dtype=np.float64)
+    B, H, S, D = q.shape
+    rows = probe_rows(S, n_rows)
+    from .attention import attention_rows
+    ref = quantize_qk(q, k)
+    exact = attention_rows(q, k, v, rows, scale)
+    quant = attention_int8(ref["q_codes"], ref["q_scale"], ref["k_codes"], ref["k_scale"], v,
+                           scale, rows=rows)
+    num = ((quant - exact) ** 2).sum(axis=(2, 3))
+    den = (exact ** 2).sum(axis=(2, 3))
+    return float(np.sqrt(num.sum() / den.sum())), np.sqrt(num / den)

@@ -497,3 +497,55 @@ def test_generator_deterministic_and_shaped():
         np.testing.assert_array_equal(x, y)
     qf = datagen.bf16_to_f64(a[0])
     assert abs(qf.mean()) < 0.02 and abs(qf.std() - 1) < 0.02
+
+
+# ---- quantization-error probe ----------------------------------------------------------------
+
+def test_probe_rows_are_bin_midpoints():
+    for S, R in [(1, 1), (7, 7), (10, 1), (10, 3), (4608, 256), (118800, 256), (129, 64)]:
+        rows = oracle.probe_rows(S, R)
+        assert rows.size == R and np.all(np.diff(rows) > 0)
+        for i, r in enumerate(rows):
+            # r is the floor of the midpoint of bin i of [0, S) split into R equal bins
+            assert Fraction(i * S, R) <= r < Fraction((i + 1) * S, R)
+            assert r == int(Fraction((2 * i + 1) * S, 2 * R))
+    assert list(oracle.probe_rows(5, 5)) == [0, 1, 2, 3, 4]
+    assert list(oracle.probe_rows(9, 1)) == [4]
+
+
+def test_probe_error_zero_when_quantization_is_exact():
+    # integer Q, K with +-127 in every block and zero K column sums: codes equal the values
+    rng = np.random.default_rng(31)
+    S, D = 256, 16
+    q = rng.integers(-126, 127, (1, 2, S, D)).astype(np.float64)
+    q[:, :, ::128, 0] = 127
+    half = rng.integers(-126, 127, (1, 2, S // 2, D)).astype(np.float64)
+    half[:, :, ::32, 1] = 127
+    k = np.concatenate([half, -half], axis=2)
+    v = _bf(rng.standard_normal((1, 2, S, D)))
+    overall, per_head = oracle.quant_probe_error(q, k, v, 32, scale=1 / 64.0)
+    assert overall <= 1e-12 and np.all(per_head <= 1e-12)
+
+
+def test_probe_error_brute_force_aggregation():
+    rng = np.random.default_rng(32)
+    B, H, S, D, R = 2, 2, 150, 16, 7
+    q, k, v = (_bf(rng.standard_normal((B, H, S, D))) for _ in range(3))
+    overall, per_head = oracle.quant_probe_error(q, k, v, R)
+    full_exact = oracle.attention(q, k, v)
+    qq = oracle.quantize_qk(q, k)
+    full_quant = oracle.attention_int8(qq["q_codes"], qq["q_scale"], qq["k_codes"], qq["k_scale"], v)
+    tot_num = tot_den = 0.0
+    for b in range(B):
+        for h in range(H):
+            num = den = 0.0
+            for i in range(R):
+                row = ((2 * i + 1) * S) // (2 * R)
+                for d in range(D):
+                    num += (full_quant[b, h, row, d] - full_exact[b, h, row, d]) ** 2
+                    den += full_exact[b, h, row, d] ** 2
+            assert abs(per_head[b, h] - math.sqrt(num / den)) <= 1e-12
+            tot_num += num
+            tot_den += den
+    assert abs(overall - math.sqrt(tot_num / tot_den)) <= 1e-12
+    assert 1e-3 < overall < 0.1   # int8 error of Gaussian inputs: small but not zero
