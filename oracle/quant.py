@@ -166,10 +166,12 @@ def log_sum_exp_int8(q_codes, q_scale, k_codes, k_scale, scale: float | None = N
 
 
 def probe_rows(S: int, n_rows: int) -> np.ndarray:
-    """The query rows a quantization-error probe samples: row i = floor((2i + 1) S / (2 n_rows)),
-    the midpoint of the i-th of n_rows equal bins of [0, S) (this library's choice)."""
-    i = np.arange(n_rows, dtype=np.int64)
-    return (2 * i + 1) * S // (2 * n_rows)
+    """The query rows a quantization-error probe samples (this library's choice): with
+    step = floor(S / n_rows), row i = floor(step / 2) + i * step, the middle row of the i-th of
+    n_rows bins of step consecutive rows (the upper of the two middle rows when step is even;
+    the last S - n_rows * step rows are never sampled)."""
+    step = S // n_rows
+    return step // 2 + np.arange(n_rows, dtype=np.int64) * step
 
 
 def quant_probe_error(q, k, v, n_rows: int, scale: float | None = None):

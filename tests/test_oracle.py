@@ -501,16 +501,20 @@ def test_generator_deterministic_and_shaped():
 
 # ---- quantization-error probe ----------------------------------------------------------------
 
-def test_probe_rows_are_bin_midpoints():
+def test_probe_rows_are_bin_middles():
     for S, R in [(1, 1), (7, 7), (10, 1), (10, 3), (4608, 256), (118800, 256), (129, 64)]:
         rows = oracle.probe_rows(S, R)
-        assert rows.size == R and np.all(np.diff(rows) > 0)
+        step = S // R
+        assert rows.size == R and np.all(np.diff(rows) == step) and rows[-1] < S
         for i, r in enumerate(rows):
-            # r is the floor of the midpoint of bin i of [0, S) split into R equal bins
-            assert Fraction(i * S, R) <= r < Fraction((i + 1) * S, R)
-            assert r == int(Fraction((2 * i + 1) * S, 2 * R))
+            # bin i holds rows [i step, (i + 1) step); r is its middle row (the upper of the two
+            # middle rows when step is even)
+            lo, hi = i * step, (i + 1) * step
+            assert lo <= r < hi and (r - lo) - (hi - 1 - r) in (0, 1)
     assert list(oracle.probe_rows(5, 5)) == [0, 1, 2, 3, 4]
     assert list(oracle.probe_rows(9, 1)) == [4]
+    assert list(oracle.probe_rows(10, 3)) == [1, 4, 7]
+    assert list(oracle.probe_rows(118800, 256)[:3]) == [232, 696, 1160]
 
 
 def test_probe_error_zero_when_quantization_is_exact():
@@ -540,7 +544,7 @@ def test_probe_error_brute_force_aggregation():
         for h in range(H):
             num = den = 0.0
             for i in range(R):
-                row = ((2 * i + 1) * S) // (2 * R)
+                row = (S // R) // 2 + i * (S // R)
                 for d in range(D):
                     num += (full_quant[b, h, row, d] - full_exact[b, h, row, d]) ** 2
                     den += full_exact[b, h, row, d] ** 2
