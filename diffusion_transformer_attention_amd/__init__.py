@@ -11,6 +11,7 @@ Entry points (same names as the C ABI in include/ditattn.h):
   attn_fwd_bf16(q, k, v, out=None, scale=None) -> out
   attn_fwd_int8qk(q, k, v, out=None, scale=None, workspace=None) -> out
   resid_rel_l1(a, b, out=None, workspace=None) -> out (fp32 device scalar, shape [1])
+  attn_quant_probe(q, k, v, o_q, n_rows=256, scale=None) -> err (fp32 [1 + B*H])
   fbcache_decide(resid, prev_resid, state, config, workspace=None) -> state
   resid_add(a, b, out=None) -> out;  resid_sub(a, b, out=None) -> out
 
@@ -34,6 +35,7 @@ import torch  # loaded first: the library then binds to the HIP runtime torch al
 __all__ = ["attn_fwd_bf16", "attn_fwd_int8qk", "resid_rel_l1", "int8qk_workspace",
            "int8qk_views", "int8qk_workspace_bytes", "rel_l1_workspace_bytes", "fbcache_decide",
            "resid_add", "resid_sub", "FBCacheConfig", "fbcache_state", "fbcache_state_values",
+           "attn_quant_probe", "quant_probe_workspace_bytes", "quant_probe_views",
            "lib", "LIB_PATH", "DitAttnError"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libditattn.so")
@@ -88,6 +90,12 @@ def lib() -> ctypes.CDLL:
     L.resid_rel_l1_workspace_bytes.restype = sz
     L.resid_rel_l1.argtypes = [vp, vp, i64, vp, vp, sz, vp]
     L.resid_rel_l1.restype = i
+    L.attn_quant_probe_splits.argtypes = [i, i, i, i, i]
+    L.attn_quant_probe_splits.restype = i
+    L.attn_quant_probe_workspace_bytes.argtypes = [i, i, i, i, i]
+    L.attn_quant_probe_workspace_bytes.restype = sz
+    L.attn_quant_probe.argtypes = [vp, vp, vp, vp, i, p64, i, i, i, i, f, i, vp, vp, sz, vp]
+    L.attn_quant_probe.restype = i
     L.fbcache_decide.argtypes = [vp, vp, i64, ctypes.POINTER(FBCacheConfig), vp, vp, sz, vp]
     L.fbcache_decide.restype = i
     L.resid_add.argtypes = [vp, vp, vp, i64, vp]
@@ -257,6 +265,50 @@ def resid_rel_l1(a, b, out=None, workspace=None):
     _check(lib().resid_rel_l1(_ptr(a), _ptr(b), n, _ptr(out), _ptr(workspace), workspace.numel(),
                               _stream(a)))
     return out
+
+
+# ---- quantization-error probe ---------------------------------------------------------------
+
+def quant_probe_workspace_bytes(B, H, S, D, n_rows) -> int:
+    return int(lib().attn_quant_probe_workspace_bytes(B, H, S, D, n_rows))
+
+
+def quant_probe_views(workspace, B, H, S, D, n_rows) -> dict:
+    """Views of the probe workspace: the chunk outputs `part` [ns, B, H, n_rows, D], their
+    log-sum-exps `lse` [ns, B, H, n_rows] and the key range [start, stop) of each chunk."""
+    ns = int(lib().attn_quant_probe_splits(B, H, S, D, n_rows))
+    if ns == 0:
+        raise DitAttnError(-1, "invalid shape or n_rows")
+    al = lambda x: (x + 255) // 256 * 256  # noqa: E731
+    n_part = ns * B * H * n_rows * D
+    part = workspace[:n_part * 4].view(torch.float32).view(ns, B, H, n_rows, D)
+    off = al(n_part * 4)
+    lse = workspace[off:off + ns * B * H * n_rows * 4].view(torch.float32).view(ns, B, H, n_rows)
+    L = (-(-S // ns) + 63) // 64 * 64
+    return {"part": part, "lse": lse, "chunks": [(c * L, min(S, (c + 1) * L)) for c in range(ns)]}
+
+
+def attn_quant_probe(q, k, v, o_q, n_rows=256, scale=None, err=None, workspace=None):
+    """Relative L2 error of a quantized call's output o_q (fp32 or bf16 [B,H,S,D] view) against
+    the bf16 path on n_rows evenly spaced query rows per (b, h).  Returns err (fp32 device
+    tensor [1 + B*H]): err[0] over all rows, err[1 + b*H + h] per head."""
+    B, H, S, D = _qkv_shape(q, k, v)
+    if o_q.dtype not in (torch.float32, torch.bfloat16) or tuple(o_q.shape) != (B, H, S, D) \
+            or o_q.stride(3) != 1 or o_q.device != q.device:
+        raise ValueError(f"o_q must be a fp32 or bf16 tensor of shape {(B, H, S, D)} on q's device")
+    scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    if err is None:
+        err = torch.empty(1 + B * H, dtype=torch.float32, device=q.device)
+    if workspace is None:
+        n = quant_probe_workspace_bytes(B, H, S, D, n_rows)
+        if n == 0:
+            raise DitAttnError(-1, "invalid shape or n_rows")
+        workspace = torch.empty(n, dtype=torch.uint8, device=q.device)
+    _check(lib().attn_quant_probe(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(o_q), OUT_BF16 if o_q.dtype == torch.bfloat16 else OUT_F32,
+        _strides_arg(q, k, v, o_q), B, H, S, D, scale, n_rows, _ptr(err), _ptr(workspace),
+        workspace.numel(), _stream(q)))
+    return err
 
 
 # ---- First Block Cache ----------------------------------------------------------------------

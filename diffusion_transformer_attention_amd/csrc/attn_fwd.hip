@@ -105,18 +105,30 @@ __device__ __forceinline__ int vswz(int row, int ch) {
 // An empty asm that the compiler must assume redefines x (a VGPR value).
 __device__ __forceinline__ void opaque(uint32_t& x) { asm volatile("" : "+v"(x)); }
 
+// N no-ops, executed once: they only move the code after them by 4 N bytes.
+template <int N>
+__device__ __forceinline__ void pad_nops() {
+  if constexpr (N > 0) {
+    asm volatile("s_nop 0");
+    pad_nops<N - 1>();
+  }
+}
+
 // Sizes and strides of one call (passed by value into the kernel's scalar argument segment).
 // Strides are in elements of the respective tensor; the channel axis is contiguous.  The
 // pointers stay separate __restrict__ arguments: only then may the per-tile K scale be read
 // with a scalar load, which does not wait for the K/V tile copies in flight.
 struct KArgs {
   int64_t qsb, qsh, qss, ksb, ksh, kss, vsb, vsh, vss, osb, osh, oss;
-  int H, S, n_qt;
+  int H;
+  int Sq;                  // query rows per (b, h)
+  int Sk;                  // keys per (b, h)
+  int n_qt;
   float c;                 // scale * log2(e)
   int o_bf16;
 };
 
-// q, k: bf16 Q and K, or the int8 codes; v: bf16 V; o: fp32 or bf16 O; lse: fp32 [B, H, S]
+// q, k: bf16 Q and K, or the int8 codes; v: bf16 V; o: fp32 or bf16 O; lse: fp32 [B, H, Sq]
 // natural-log normalisers, or null; q_scale / k_scale: the int8 path's per-block scales.
 // At D = 64 the wave count per SIMD is capped at two as well: one 8-wave workgroup per CU is
 // the design and a third wave slot could not hold a second workgroup, yet aiming for three
@@ -128,7 +140,7 @@ void attn_fwd_kernel(const uint8_t* __restrict__ qp, const uint8_t* __restrict__
                      const uint8_t* __restrict__ vp, uint8_t* __restrict__ op,
                      float* __restrict__ lse, const float* __restrict__ q_scale,
                      const float* __restrict__ k_scale, const KArgs a) {
-  const int S = a.S, n_qt = a.n_qt;
+  const int Sq = a.Sq, Sk = a.Sk, n_qt = a.n_qt;
   const float c = a.c;
   using T = Tile<D, INT8, NW>;
   constexpr int kThreads = T::NT;
@@ -160,22 +172,22 @@ void attn_fwd_kernel(const uint8_t* __restrict__ qp, const uint8_t* __restrict__
   const uint8_t* kh = kp + (bb * a.ksb + hd * a.ksh) * EB;   // first key row of this (b, h)
   const uint8_t* vh = vp + (bb * a.vsb + hd * a.vsh) * 2;
   const int64_t krs = a.kss * EB, vrs = a.vss * 2;            // bytes between key / value rows
-  const int nkt = (S + kBK - 1) / kBK;
+  const int nkt = (Sk + kBK - 1) / kBK;
 
   // ---- Q fragment: B operand; lane holds query q, bytes [32f + 16hh, +16) of its row -------
   const int q = qt * kBQ + wave * 32 + l32;
   u32x4 qf[T::NQF];
   {
-    const uint8_t* qrow = qp + (bb * a.qsb + hd * a.qsh + (int64_t)min(q, S - 1) * a.qss) * EB;
+    const uint8_t* qrow = qp + (bb * a.qsb + hd * a.qsh + (int64_t)min(q, Sq - 1) * a.qss) * EB;
 #pragma unroll
     for (int f = 0; f < T::NQF; ++f) {
       const u32x4 x = *reinterpret_cast<const u32x4*>(qrow + f * 32 + hh * 16);
-      qf[f] = (q < S) ? x : u32x4{0u, 0u, 0u, 0u};
+      qf[f] = (q < Sq) ? x : u32x4{0u, 0u, 0u, 0u};
     }
   }
   float cq = c;
   if constexpr (INT8) {
-    const int nqb = (S + kQBlock - 1) / kQBlock;
+    const int nqb = (Sq + kQBlock - 1) / kQBlock;  // (the int8 path never samples: Sq = Sk)
     cq = q_scale[(size_t)bh * nqb + (qt * kBQ + wave * 32) / kQBlock] * c;
   }
 
@@ -203,13 +215,13 @@ void attn_fwd_kernel(const uint8_t* __restrict__ qp, const uint8_t* __restrict__
     const int key = p / T::VCH, pch = p % T::VCH;
     vofl[r] = (uint32_t)(key * vrs) + vswz<D>(key, pch) * 16;
   }
-  // First row of tile kt: kt * kBK, except a ragged last tile, which starts at S - kBK
-  // (S >= kBK whenever more than one tile exists).  Tiles of K and of V are each loaded once,
+  // First row of tile kt: kt * kBK, except a ragged last tile, which starts at Sk - kBK
+  // (Sk >= kBK whenever more than one tile exists).  Tiles of K and of V are each loaded once,
   // in order, so their base addresses advance by one tile per load (uniform, in SGPRs).
   const uint8_t* k_next = kh;
   const uint8_t* v_next = vh;
-  const uint8_t* const k_last = kh + (int64_t)max(S - kBK, 0) * krs;
-  const uint8_t* const v_last = vh + (int64_t)max(S - kBK, 0) * vrs;
+  const uint8_t* const k_last = kh + (int64_t)max(Sk - kBK, 0) * krs;
+  const uint8_t* const v_last = vh + (int64_t)max(Sk - kBK, 0) * vrs;
   const int64_t k_step = kBK * krs, v_step = kBK * vrs;
   // The offsets are redefined (by an empty asm) at the top of every loop iteration, so their
   // zero extension cannot be hoisted out of the loop and each address is selected as scalar
@@ -234,21 +246,21 @@ void attn_fwd_kernel(const uint8_t* __restrict__ qp, const uint8_t* __restrict__
       __builtin_amdgcn_global_load_lds(tb + off, (lds_void*)(dst + (r * kThreads + wave_u * 64) * 16), 16, 0, 0);
     }
   };
-  // the single tile of a sequence shorter than kBK: rows clamped to S - 1
+  // the single tile of a sequence shorter than kBK: rows clamped to Sk - 1
   auto load_short = [&](uint8_t* kdst, uint8_t* vdst) {
 #pragma unroll
     for (int r = 0; r < T::KLD; ++r) {
       if (T::KPART && wave_u * 64 >= T::KBYTES / 16) break;
       const int p = r * kThreads + tid;
       const int key = p / T::KCH, pch = p % T::KCH;
-      const uint32_t off = (uint32_t)(min(key, S - 1) * krs) + kswz<D, INT8>(key, pch) * 16;
+      const uint32_t off = (uint32_t)(min(key, Sk - 1) * krs) + kswz<D, INT8>(key, pch) * 16;
       __builtin_amdgcn_global_load_lds(kh + off, (lds_void*)(kdst + (r * kThreads + wave_u * 64) * 16), 16, 0, 0);
     }
 #pragma unroll
     for (int r = 0; r < T::VLD; ++r) {
       const int p = r * kThreads + tid;
       const int key = p / T::VCH, pch = p % T::VCH;
-      const uint32_t off = (uint32_t)(min(key, S - 1) * vrs) + vswz<D>(key, pch) * 16;
+      const uint32_t off = (uint32_t)(min(key, Sk - 1) * vrs) + vswz<D>(key, pch) * 16;
       __builtin_amdgcn_global_load_lds(vh + off, (lds_void*)(vdst + (r * kThreads + wave_u * 64) * 16), 16, 0, 0);
     }
   };
@@ -322,13 +334,13 @@ void attn_fwd_kernel(const uint8_t* __restrict__ qp, const uint8_t* __restrict__
     }
   };
 
-  // Masks the keys tile jt does not own (a partial last tile: keys outside [jt * kBK, S) were
+  // Masks the keys tile jt does not own (a partial last tile: keys outside [jt * kBK, Sk) were
   // already seen in tile jt - 1, or lie past the end).  In tile-local key numbers the valid
   // range is [lo, hi); the empty asm keeps the comparisons inside the rarely taken branch.
   auto mask_tile = [&](int jt, float (&s)[32]) __attribute__((always_inline)) {
-    if (jt == nkt - 1 && (S % kBK) != 0) {
-      const int t0 = max(S - kBK, 0);  // the tile's first row
-      int lo = jt * kBK - t0 - 4 * hh, hi = S - t0 - 4 * hh;
+    if (jt == nkt - 1 && (Sk % kBK) != 0) {
+      const int t0 = max(Sk - kBK, 0);  // the tile's first row
+      int lo = jt * kBK - t0 - 4 * hh, hi = Sk - t0 - 4 * hh;
       asm volatile("" : "+v"(lo), "+v"(hi));
 #pragma unroll
       for (int r = 0; r < 32; ++r) {
@@ -437,7 +449,7 @@ void attn_fwd_kernel(const uint8_t* __restrict__ qp, const uint8_t* __restrict__
   };
 
   // ---- prologue: S[0], S[1] and P[0] computed; K[2] and V[0] resident ---------------------
-  if (S < kBK) {
+  if (Sk < kBK) {
     load_short(kbuf_0, vbuf_0);
   } else {
     load_k(0, kbuf_0);
@@ -462,6 +474,12 @@ void attn_fwd_kernel(const uint8_t* __restrict__ qp, const uint8_t* __restrict__
   __builtin_amdgcn_s_waitcnt(0x0F70);
   __syncthreads();
 
+  // Where the main loop lands in the instruction stream matters: shifting the same loop by
+  // 4-byte steps moved the long-video int8 call by up to 3% (shifts that are a multiple of 8
+  // bytes from the unpadded placement were the slow ones) and the bf16 call by up to 1%.
+  // These pads are the measured best for this loop and compiler.
+  pad_nops<INT8 ? 1 : 3>();
+
   // stage j reads S[j+1] and writes S[j+2]; consumes P[j] and produces P[j+1]
   int j = 0;
   for (; j + 1 < nkt; j += 2) {
@@ -477,7 +495,7 @@ void attn_fwd_kernel(const uint8_t* __restrict__ qp, const uint8_t* __restrict__
   // ---- epilogue: O = O_acc / l (fp32 or bf16), and optionally the row's log-sum-exp ------
   const float l_tot = xor32_sum(l_run);
   const float inv = 1.f / l_tot;
-  if (q < S) {
+  if (q < Sq) {
     const int64_t orow = bb * a.osb + hd * a.osh + (int64_t)q * a.oss;  // element offset
     if (a.o_bf16) {
       uint16_t* o16 = reinterpret_cast<uint16_t*>(op) + orow;
@@ -503,7 +521,7 @@ void attn_fwd_kernel(const uint8_t* __restrict__ qp, const uint8_t* __restrict__
     }
     // log sum_j exp(scale * s_j) = (m + log2 l) * ln 2: the weights are 2^(scale log2e s - m)
     if (lse != nullptr && hh == 0)
-      lse[(int64_t)bh * S + q] = (m_run + __builtin_amdgcn_logf(l_tot)) * kLn2;
+      lse[(int64_t)bh * Sq + q] = (m_run + __builtin_amdgcn_logf(l_tot)) * kLn2;
   }
 }
 
@@ -517,8 +535,9 @@ hipError_t launch(const AttnCall& ac, const void* q, Strides qs, const void* k, 
   a.vsb = ac.vs.b; a.vsh = ac.vs.h; a.vss = ac.vs.s;
   a.osb = ac.os.b; a.osh = ac.os.h; a.oss = ac.os.s;
   a.H = ac.H;
-  a.S = ac.S;
-  a.n_qt = (ac.S + T::BQ - 1) / T::BQ;
+  a.Sq = ac.Sq;
+  a.Sk = ac.S;
+  a.n_qt = (ac.Sq + T::BQ - 1) / T::BQ;
   a.c = ac.scale * kLog2e;
   a.o_bf16 = ac.o_bf16 ? 1 : 0;
   const long long nwg = (long long)ac.B * ac.H * a.n_qt;

@@ -80,6 +80,7 @@ ditattn::AttnCall make_call(const void* q, const void* k, const void* v, void* o
   ac.vs = {st[6], st[7], st[8]};
   ac.os = {st[9], st[10], st[11]};
   ac.B = B; ac.H = H; ac.S = S; ac.D = D; ac.scale = scale;
+  ac.Sq = S;
   return ac;
 }
 
@@ -217,6 +218,43 @@ int resid_rel_l1(const void* a, const void* b, int64_t n, float* out, void* work
     return DITATTN_EWORKSPACE;
   return status_of(ditattn::launch_rel_l1(a, b, n, out, static_cast<double*>(workspace),
                                           static_cast<hipStream_t>(stream)));
+}
+
+int attn_quant_probe_splits(int B, int H, int S, int D, int n_rows) {
+  if (check_attn_shape(B, H, S, D) != DITATTN_OK || n_rows < 1 || n_rows > S) return 0;
+  return ditattn::probe_splits(B, H, S, n_rows);
+}
+
+size_t attn_quant_probe_workspace_bytes(int B, int H, int S, int D, int n_rows) {
+  if (check_attn_shape(B, H, S, D) != DITATTN_OK || n_rows < 1 || n_rows > S) return 0;
+  const size_t ns = (size_t)ditattn::probe_splits(B, H, S, n_rows);
+  const size_t rows = (size_t)B * H * n_rows;
+  return align_up(ns * rows * D * sizeof(float), kSegAlign) +
+         align_up(ns * rows * sizeof(float), kSegAlign) +
+         align_up((size_t)B * H * 2 * sizeof(double), kSegAlign);
+}
+
+int attn_quant_probe(const void* q, const void* k, const void* v, const void* o_q, int o_q_dtype,
+                     const int64_t* strides, int B, int H, int S, int D, float scale, int n_rows,
+                     float* err, void* workspace, size_t workspace_bytes, void* stream) {
+  const int st = check_ex_args(q, k, v, o_q, o_q_dtype, nullptr, strides, B, H, S, D, scale);
+  if (st != DITATTN_OK) return st;
+  if (n_rows < 1 || n_rows > S || !err || !aligned(err, 4)) return DITATTN_EINVAL;
+  // the sampled rows are a strided view of q: its token stride times S / n_rows
+  if (strides[2] * (S / n_rows) >= (int64_t(1) << 24)) return DITATTN_EINVAL;
+  const size_t need = attn_quant_probe_workspace_bytes(B, H, S, D, n_rows);
+  if (!workspace || !aligned(workspace, kSegAlign) || workspace_bytes < need) return DITATTN_EWORKSPACE;
+  const size_t ns = (size_t)ditattn::probe_splits(B, H, S, n_rows);
+  const size_t rows = (size_t)B * H * n_rows;
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  float* part = reinterpret_cast<float*>(ws);
+  float* lse = reinterpret_cast<float*>(ws + align_up(ns * rows * D * sizeof(float), kSegAlign));
+  double* sums = reinterpret_cast<double*>(reinterpret_cast<uint8_t*>(lse) +
+                                           align_up(ns * rows * sizeof(float), kSegAlign));
+  ditattn::AttnCall base = make_call(q, k, v, nullptr, false, nullptr, strides, B, H, S, D, scale);
+  return status_of(ditattn::launch_quant_probe(base, o_q, o_q_dtype == DITATTN_OUT_BF16,
+                                               base.os, n_rows, err, part, lse, sums,
+                                               static_cast<hipStream_t>(stream)));
 }
 
 int fbcache_decide(const void* resid, const void* prev_resid, int64_t n,

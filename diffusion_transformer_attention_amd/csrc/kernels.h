@@ -17,7 +17,9 @@ struct Strides {
   int64_t b, h, s;
 };
 
-// One attention call: q, k, v bf16 views, o fp32 or bf16 view, optional lse fp32 [B, H, S].
+// One attention call: q, k, v bf16 views, o fp32 or bf16 view, optional lse fp32 [B, H, Sq].
+// S keys and Sq query rows per (b, h) (Sq = S except for the quantization probe's sampled
+// rows; the int8 path always has Sq = S).
 struct AttnCall {
   const void* q;
   const void* k;
@@ -28,6 +30,7 @@ struct AttnCall {
   Strides qs, ks, vs, os;
   int B, H, S, D;
   float scale;
+  int Sq;
 };
 
 hipError_t launch_attn_bf16(const AttnCall& ac, hipStream_t stream);
@@ -58,6 +61,18 @@ hipError_t launch_rel_l1(const void* a, const void* b, int64_t n, float* out, do
 hipError_t launch_fbcache_decide(const void* resid, const void* prev_resid, int64_t n,
                                  const ditattn_fbcache_config& cfg, ditattn_fbcache_state* state,
                                  double* partial, hipStream_t stream);
+
+// Key chunks the quantization probe splits each (b, h) into for R sampled rows.
+int probe_splits(int B, int H, int S, int R);
+
+// The quantization probe: bf16 attention of R rows per (b, h), rows step/2 + i step with
+// step = S / R (q, k, v, scale and their strides from `base`), in probe_splits chunks of keys with their lse
+// into part (fp32 [ns][B*H][R][D]) and lse (fp32 [ns][B*H][R]); then err[1 + bh] (and err[0]
+// over all) = sqrt(sum |o_q - o|^2 / sum |o|^2) against the quantized output o_q on those rows.
+// sums: B*H double pairs.
+hipError_t launch_quant_probe(const AttnCall& base, const void* o_q, bool o_q_bf16, Strides oqs,
+                              int R, float* err, float* part, float* lse, double* sums,
+                              hipStream_t stream);
 
 // out = bf16(a + b) (SUB: a - b) elementwise over n bf16 values, each rounded once.
 hipError_t launch_resid_addsub(const void* a, const void* b, void* out, int64_t n, bool sub,

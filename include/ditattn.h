@@ -155,6 +155,41 @@ DITATTN_API size_t resid_rel_l1_workspace_bytes(int64_t n);
 DITATTN_API int resid_rel_l1(const void* a, const void* b, int64_t n, float* out,
                  void* workspace, size_t workspace_bytes, void* stream);
 
+/* ---- quantization-error probe -----------------------------------------------------------
+ *
+ * Which attention layers may run quantized: the "TMAP image-to-video inference acceleration"
+ * page (section on preserving video quality) keeps the layers whose quantized attention
+ * errs most in full precision.  attn_quant_probe measures that error for one call: the bf16
+ * path's output on n_rows evenly spaced query rows per (b, h) against the output o_q of a
+ * quantized call (attn_fwd_int8qk[_ex]) on the same inputs, at about n_rows / S of a bf16
+ * call's work.  Sampled row i = step / 2 + i * step with step = floor(S / n_rows): the middle
+ * row of the i-th bin of step rows (integer division). */
+
+/* Number of key chunks ns the probe splits each (b, h) into (0 if the arguments are invalid):
+ * enough to give the few sampled rows work for every CU. */
+DITATTN_API int attn_quant_probe_splits(int B, int H, int S, int D, int n_rows);
+
+/* Workspace of attn_quant_probe, in bytes (0 if the shape or n_rows is invalid).  Layout, each
+ * segment on a 256-byte boundary: fp32 [ns][B*H][n_rows][D] chunk outputs, fp32
+ * [ns][B*H][n_rows] chunk log-sum-exps (chunk c holds keys [c L, min(S, (c+1) L)),
+ * L = ceil(ceil(S / ns) / 64) * 64), fp64 [B*H][2] per-head sums.  After a call the chunk
+ * segments hold the bf16 path's partial results for the sampled rows. */
+DITATTN_API size_t attn_quant_probe_workspace_bytes(int B, int H, int S, int D, int n_rows);
+
+/*   q, k, v, strides, B, H, S, D, scale : the quantized call's inputs, as in attn_fwd_bf16_ex
+ *   o_q, o_q_dtype                      : its output (DITATTN_OUT_F32 / _BF16), strides[9..11]
+ *   n_rows                              : 1 <= n_rows <= S
+ *   err       : fp32 device array of 1 + B*H values, written with
+ *               err[0]          = sqrt(sum |o_q - o|^2 / sum |o|^2) over all sampled rows,
+ *               err[1 + b*H + h] the same for head (b, h), o = the bf16 path's output
+ *   workspace : >= attn_quant_probe_workspace_bytes(B, H, S, D, n_rows) bytes, 256-byte aligned
+ * Errors as attn_fwd_bf16_ex, plus DITATTN_EINVAL for n_rows out of range, a NULL err, or
+ * q's token stride times step reaching 2^24 (the sampled rows are read as a strided view). */
+DITATTN_API int attn_quant_probe(const void* q, const void* k, const void* v, const void* o_q,
+                                 int o_q_dtype, const int64_t* strides, int B, int H, int S,
+                                 int D, float scale, int n_rows, float* err, void* workspace,
+                                 size_t workspace_bytes, void* stream);
+
 /* ---- First Block Cache ------------------------------------------------------------------
  *
  * A denoising step of a DiT may skip its remaining transformer blocks when the residual its

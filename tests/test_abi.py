@@ -31,9 +31,10 @@ def declared_functions():
 def test_header_declares_the_three_calls():
     names = declared_functions()
     for n in ("attn_fwd_bf16", "attn_fwd_int8qk", "resid_rel_l1", "attn_fwd_bf16_ex",
-              "attn_fwd_int8qk_ex", "fbcache_decide", "resid_add", "resid_sub"):
+              "attn_fwd_int8qk_ex", "fbcache_decide", "resid_add", "resid_sub",
+              "attn_quant_probe"):
         assert n in names
-    assert len(names) == 12
+    assert len(names) == 15
 
 
 def test_library_exports_every_declared_symbol(L):
@@ -163,6 +164,36 @@ def test_rel_l1_argument_errors(L):
     assert L.resid_rel_l1(FAKE + 2, FAKE + 0x100, 100, FAKE + 0x1000, FAKE + 0x2000, need, None) == EINVAL
     assert L.resid_rel_l1(FAKE, FAKE + 0x100, 100, FAKE + 0x1000, None, need, None) == EWS
     assert L.resid_rel_l1(FAKE, FAKE + 0x100, 100, FAKE + 0x1000, FAKE + 0x2000, need - 1, None) == EWS
+
+
+def test_quant_probe_workspace_and_errors(L):
+    assert L.attn_quant_probe_splits(1, 24, 118800, 128, 256) == 10   # 24 workgroups per chunk
+    assert L.attn_quant_probe_splits(1, 2, 1000, 64, 100) == 1        # chunks >= ~1024 keys
+    assert L.attn_quant_probe_splits(1, 1, 1 << 20, 64, 64) == 16     # at most 16
+    assert L.attn_quant_probe_splits(1, 1, 100, 64, 101) == 0
+    assert L.attn_quant_probe_workspace_bytes(1, 24, 4608, 128, 0) == 0
+    assert L.attn_quant_probe_workspace_bytes(1, 24, 4608, 128, 4609) == 0
+    assert L.attn_quant_probe_workspace_bytes(1, 24, 4608, 96, 64) == 0
+    need = L.attn_quant_probe_workspace_bytes(1, 2, 4096, 64, 64)
+    # at least the chunk outputs of one split and the per-head sums
+    assert need >= 1 * 2 * 64 * 64 * 4 + 2 * 16 and need % 256 == 0
+    st = (ctypes.c_int64 * 12)(*_contig(2, 4096, 64))
+    Q, K, V, O, E, W = FAKE, FAKE + 0x1000, FAKE + 0x2000, FAKE + 0x3000, FAKE + 0x4000, FAKE + 0x8000
+
+    def call(n_rows=64, err=E, ws=W, ws_bytes=need, o=O, dtype=0, strides=st, D=64):
+        return L.attn_quant_probe(Q, K, V, o, dtype, strides, 1, 2, 4096, D, 0.125, n_rows, err,
+                                  ws, ws_bytes, None)
+    assert call(n_rows=0) == EINVAL
+    assert call(n_rows=4097) == EINVAL
+    assert call(err=None) == EINVAL
+    assert call(err=E + 2) == EINVAL
+    assert call(o=Q) == EINVAL
+    assert call(dtype=3) == EINVAL
+    assert call(strides=None) == EINVAL
+    assert call(D=80) == EUNSUP
+    assert call(ws=None) == EWS
+    assert call(ws_bytes=need - 1) == EWS
+    assert call(ws=W + 16) == EWS
 
 
 def test_fbcache_struct_layout_matches_header():
