@@ -167,6 +167,25 @@ def time_fbcache(torch, dta, stream, ev, a, b, iters=20):
     return res
 
 
+def time_probe(torch, dta, stream, ev, q, k, v, o_int8, n_rows=256, iters=10):
+    """Quantization-error probe on the long-video call: n_rows rows per head, ms per call."""
+    B, H, S, D = q.shape
+    ws = torch.empty(dta.quant_probe_workspace_bytes(B, H, S, D, n_rows), dtype=torch.uint8,
+                     device="cuda")
+    err = torch.empty(1 + B * H, dtype=torch.float32, device="cuda")
+    fn = lambda: dta.attn_quant_probe(q, k, v, o_int8, n_rows=n_rows, err=err, workspace=ws)  # noqa: E731
+    fn()
+    e0, e1 = ev(), ev()
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(iters):
+        fn()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return {"ms": e0.elapsed_time(e1) / iters, "rows_per_head": n_rows,
+            "err_int8_vs_bf16": float(err[0].item())}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -174,7 +193,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--headline-only", action="store_true",
-                    help="skip the extra timings (S=4608 attention, First Block Cache calls): "
+                    help="skip the extra timings (S=4608 attention, First Block Cache calls, "
+                         "quantization probe): "
                          "profiling runs, one shape per kernel")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy three times (the "
@@ -260,6 +280,7 @@ def main():
     # image-DiT shape, timed separately (not part of `value`)
     img = None if args.headline_only else time_image_shape(torch, dta, stream, ev)
     fbc = None if args.headline_only else time_fbcache(torch, dta, stream, ev, a, b)
+    probe = None if args.headline_only else time_probe(torch, dta, stream, ev, q, k, v, o_int8)
 
     traffic = load_traffic()
     line = {
@@ -289,6 +310,7 @@ def main():
             "rel_l1": {"ms": ms_rl1, "gbs": rl1_gbs, "frac_hbm_peak": rl1_gbs / PEAK_HBM_GBS},
             "image_S4608": img,
             "fbcache_118800x3072": fbc,
+            "quant_probe": probe,
             "wall_s_timed": wall,
         },
     }
