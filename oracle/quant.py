@@ -30,6 +30,9 @@ The rest is this library's stated contract (the pages leave it open):
 6. Attention on the codes: s_ij = (sum_d qc_id * kc_jd) * sq[i // 128] * sk[j // 64] * scale,
    the integer dot product exact; softmax and the product with V (bf16 values) as in exact
    attention, all in fp64.
+
+The fp8 variant (end of the module) keeps rules 1-3 and 6 and replaces 4-5 by e4m3 codes:
+scale = amax / 448 and one rounding of x / scale to the nearest e4m3 value.
 """
 from __future__ import annotations
 
@@ -194,3 +197,90 @@ def quant_probe_error(q, k, v, n_rows: int, scale: float | None = None):
     num = ((quant - exact) ** 2).sum(axis=(2, 3))
     den = (exact ** 2).sum(axis=(2, 3))
     return float(np.sqrt(num.sum() / den.sum())), np.sqrt(num / den)
+
+
+# ---- fp8 (OCP e4m3) codes ---------------------------------------------------------------------
+#
+# The same steps with fp8 codes instead of int8 (this library's fp8 contract; the pages run
+# their linear layers in fp8 and their attention in 8 bits):
+#   scale = amax / 448 (IEEE fp32 division; 448 is the largest finite e4m3 value), 1.0 if
+#   amax == 0; code = e4m3(clamp(fl32(x / scale), -448, 448)), rounded once to nearest even.
+# e4m3 (OCP "E4M3FN"): 1 sign, 4 exponent bits (bias 7), 3 fraction bits; normal values
+# (1 + m/8) 2^(e-7) for e = 1..15 (e = 15, m = 7 is NaN, so the largest is 448); subnormal
+# values m/8 * 2^-6; no infinities.
+
+E4M3_MAX = 448.0
+
+
+def e4m3_value(codes) -> np.ndarray:
+    """fp64 values of e4m3 codes (uint8); NaN for the two NaN codes."""
+    c = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+    sign = np.where(c & 0x80, -1.0, 1.0)
+    e = (c >> 3) & 0xF
+    m = c & 0x7
+    mag = np.where(e == 0, m / 8.0 * 2.0 ** -6, (1.0 + m / 8.0) * 2.0 ** (e - 7.0))
+    mag = np.where((e == 15) & (m == 7), np.nan, mag)
+    return sign * mag
+
+
+def _e4m3_table():
+    vals = e4m3_value(np.arange(128, dtype=np.uint8))   # non-negative codes 0..127
+    return vals[:127]                                    # drop the NaN code 0x7F
+
+
+def e4m3_round(x) -> np.ndarray:
+    """Round fp64 values with |x| <= 448 to the nearest e4m3 value (ties to the even code,
+    i.e. the one with an even fraction field); returns uint8 codes."""
+    x = np.asarray(x, dtype=np.float64)
+    if np.any(~(np.abs(x) <= E4M3_MAX)):
+        raise ValueError("e4m3_round takes finite values of magnitude <= 448")
+    grid = _e4m3_table()                 # increasing, codes 0..126
+    a = np.abs(x)
+    hi = np.searchsorted(grid, a, side="left")        # first grid value >= a
+    hi = np.minimum(hi, grid.size - 1)
+    lo = np.maximum(hi - 1, 0)
+    d_lo = a - grid[lo]
+    d_hi = grid[hi] - a
+    pick_hi = (d_hi < d_lo) | ((d_hi == d_lo) & (hi % 2 == 0))
+    code = np.where(a == grid[hi], hi, np.where(pick_hi, hi, lo)).astype(np.int64)
+    neg = np.signbit(x) & (code != 0)
+    return (code | np.where(neg, 0x80, 0)).astype(np.uint8)
+
+
+def quantize_blocks_fp8(x, block: int):
+    """e4m3 codes (uint8 [B, H, S, D]) and per-block scales (float32 [B, H, nblk])."""
+    x = np.asarray(x, dtype=np.float32)
+    B, H, S, D = x.shape
+    nblk = -(-S // block)
+    scales = np.empty((B, H, nblk), dtype=np.float32)
+    codes = np.empty((B, H, S, D), dtype=np.uint8)
+    for t in range(nblk):
+        blk = x[:, :, t * block:min(S, (t + 1) * block)]
+        amax = np.abs(blk).max(axis=(2, 3))
+        scale = np.where(amax == 0, np.float32(1.0), amax / np.float32(E4M3_MAX)).astype(np.float32)
+        scales[:, :, t] = scale
+        q = np.clip(blk / scale[:, :, None, None], np.float32(-E4M3_MAX), np.float32(E4M3_MAX))
+        codes[:, :, t * block:min(S, (t + 1) * block)] = e4m3_round(q.astype(np.float64))
+    return codes, scales
+
+
+def quantize_qk_fp8(q, k, kmean=None):
+    """quantize_qk with e4m3 codes: same K mean and smoothing, scale = amax / 448."""
+    q = np.asarray(q, dtype=np.float64)
+    if kmean is None:
+        kmean = k_channel_mean(k)
+    qc, qs = quantize_blocks_fp8(q.astype(np.float32), Q_BLOCK)
+    kc, ks = quantize_blocks_fp8(smooth_k(k, kmean), K_BLOCK)
+    return {"k_mean": kmean, "q_codes": qc, "q_scale": qs, "k_codes": kc, "k_scale": ks}
+
+
+def attention_fp8(q_codes, q_scale, k_codes, k_scale, v, scale: float | None = None, rows=None):
+    """Attention on e4m3 codes: s_ij = (sum_d q_id k_jd) * sq * sk * scale with the code values,
+    then the exact softmax and PV, all in fp64 (as attention_int8)."""
+    return attention_int8(e4m3_value(q_codes), q_scale, e4m3_value(k_codes), k_scale, v, scale,
+                          rows=rows)
+
+
+def log_sum_exp_fp8(q_codes, q_scale, k_codes, k_scale, scale: float | None = None):
+    """log sum_j exp(s_ij) of the fp8-path scores, fp64 [B, H, S]."""
+    return log_sum_exp_int8(e4m3_value(q_codes), q_scale, e4m3_value(k_codes), k_scale, scale)
