@@ -230,7 +230,9 @@ def _e4m3_table():
 
 def e4m3_round(x) -> np.ndarray:
     """Round fp64 values with |x| <= 448 to the nearest e4m3 value (ties to the even code,
-    i.e. the one with an even fraction field); returns uint8 codes."""
+    i.e. the one with an even fraction field); returns uint8 codes.  As in any IEEE rounding
+    the sign is kept, also when the result is zero: a negative value below half the smallest
+    subnormal (and -0) gives -0, code 0x80."""
     x = np.asarray(x, dtype=np.float64)
     if np.any(~(np.abs(x) <= E4M3_MAX)):
         raise ValueError("e4m3_round takes finite values of magnitude <= 448")
@@ -243,8 +245,7 @@ def e4m3_round(x) -> np.ndarray:
     d_hi = grid[hi] - a
     pick_hi = (d_hi < d_lo) | ((d_hi == d_lo) & (hi % 2 == 0))
     code = np.where(a == grid[hi], hi, np.where(pick_hi, hi, lo)).astype(np.int64)
-    neg = np.signbit(x) & (code != 0)
-    return (code | np.where(neg, 0x80, 0)).astype(np.uint8)
+    return (code | np.where(np.signbit(x), 0x80, 0)).astype(np.uint8)
 
 
 def quantize_blocks_fp8(x, block: int):

@@ -65,12 +65,17 @@ def test_rounding_matches_torch_on_fp32_values():
     x = np.clip(x, -448, 448).astype(np.float32)
     g = np.array([float(v) for v in _grid()])
     x = np.concatenate([x, ((g[1:] + g[:-1]) / 2).astype(np.float32)])   # every tie
+    x = np.concatenate([x, np.array([-1e-5, 1e-5, -0.0, 0.0, -0.00097, -0.00098], np.float32)])
     ref = torch.from_numpy(x).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
     got = oracle.e4m3_round(x.astype(np.float64))
-    # zero: torch keeps the sign of -0.0 -> 0x80; the oracle's code for a result of zero is
-    # +0 unless the input is a negative non-zero value that rounds to zero
-    same = (got == ref) | ((oracle.e4m3_value(got) == 0) & (oracle.e4m3_value(ref) == 0))
-    assert np.all(same), x[~same][:5]
+    assert np.array_equal(got, ref), x[got != ref][:5]
+
+
+def test_rounding_keeps_the_sign_of_zero_results():
+    # half the smallest subnormal (2^-10) and below round to zero, keeping the sign
+    assert list(oracle.e4m3_round(np.array([2.0 ** -11, -2.0 ** -11, -0.0, 0.0, -2.0 ** -10,
+                                            -2.0 ** -10 * 1.01]))) == [0x00, 0x80, 0x80, 0x00,
+                                                                       0x80, 0x81]
 
 
 def test_block_quantizer_contract():
