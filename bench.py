@@ -27,7 +27,7 @@ sys.path.insert(0, ROOT)
 PEAK_BF16_TFLOPS = 2500.0    # MI355X dense bf16 MFMA
 PEAK_INT8_TOPS = 5000.0      # MI355X dense int8 MFMA
 PEAK_HBM_GBS = 8000.0        # MI355X HBM3E
-ATTN_KERNEL = "attn_fwd_kernel<128, false, 8>"
+ATTN_KERNEL = "attn_fwd_kernel<128, 0, 8>"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_bf16_longvideo_traffic.json")
 
 
@@ -167,6 +167,24 @@ def time_fbcache(torch, dta, stream, ev, a, b, iters=20):
     return res
 
 
+def time_fp8(torch, dta, stream, ev, q, k, v, o, ws, iters=3):
+    """fp8-QK attention on the long-video workload (whole call: mean, e4m3 codes, attention)."""
+    fn = lambda: dta.attn_fwd_fp8qk(q, k, v, out=o, workspace=ws)  # noqa: E731
+    fn()
+    e0, e1 = ev(), ev()
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(iters):
+        fn()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / iters
+    B, H, S, D = q.shape
+    tops = attn_flops(B, H, S, D) / (ms * 1e-3) / 1e12
+    return {"ms": ms, "tflops": tops, "frac_fp8_peak": tops / PEAK_INT8_TOPS,
+            "note": "whole call; QK on fp8 e4m3 MFMA, PV bf16"}
+
+
 def time_probe(torch, dta, stream, ev, q, k, v, o_int8, n_rows=256, iters=10):
     """Quantization-error probe on the long-video call: n_rows rows per head, ms per call."""
     B, H, S, D = q.shape
@@ -194,7 +212,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--headline-only", action="store_true",
                     help="skip the extra timings (S=4608 attention, First Block Cache calls, "
-                         "quantization probe): "
+                         "quantization probe, fp8-QK attention): "
                          "profiling runs, one shape per kernel")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy three times (the "
@@ -281,6 +299,7 @@ def main():
     img = None if args.headline_only else time_image_shape(torch, dta, stream, ev)
     fbc = None if args.headline_only else time_fbcache(torch, dta, stream, ev, a, b)
     probe = None if args.headline_only else time_probe(torch, dta, stream, ev, q, k, v, o_int8)
+    fp8 = None if args.headline_only else time_fp8(torch, dta, stream, ev, q, k, v, o_int8, ws8)
 
     traffic = load_traffic()
     line = {
@@ -311,6 +330,7 @@ def main():
             "image_S4608": img,
             "fbcache_118800x3072": fbc,
             "quant_probe": probe,
+            "fp8qk": fp8,
             "wall_s_timed": wall,
         },
     }

@@ -10,6 +10,7 @@ Entry points (same names as the C ABI in include/ditattn.h):
 
   attn_fwd_bf16(q, k, v, out=None, scale=None) -> out
   attn_fwd_int8qk(q, k, v, out=None, scale=None, workspace=None) -> out
+  attn_fwd_fp8qk(q, k, v, out=None, scale=None, workspace=None) -> out
   resid_rel_l1(a, b, out=None, workspace=None) -> out (fp32 device scalar, shape [1])
   attn_quant_probe(q, k, v, o_q, n_rows=256, scale=None) -> err (fp32 [1 + B*H])
   fbcache_decide(resid, prev_resid, state, config, workspace=None) -> state
@@ -32,7 +33,7 @@ import os
 
 import torch  # loaded first: the library then binds to the HIP runtime torch already holds
 
-__all__ = ["attn_fwd_bf16", "attn_fwd_int8qk", "resid_rel_l1", "int8qk_workspace",
+__all__ = ["attn_fwd_bf16", "attn_fwd_int8qk", "attn_fwd_fp8qk", "resid_rel_l1", "int8qk_workspace",
            "int8qk_views", "int8qk_workspace_bytes", "rel_l1_workspace_bytes", "fbcache_decide",
            "resid_add", "resid_sub", "FBCacheConfig", "fbcache_state", "fbcache_state_values",
            "attn_quant_probe", "quant_probe_workspace_bytes", "quant_probe_views",
@@ -82,6 +83,10 @@ def lib() -> ctypes.CDLL:
     L.attn_fwd_int8qk.argtypes = [vp, vp, vp, vp, i, i, i, i, f, vp, sz, vp]
     L.attn_fwd_int8qk.restype = i
     p64 = ctypes.POINTER(i64)
+    L.attn_fwd_fp8qk.argtypes = [vp, vp, vp, vp, i, i, i, i, f, vp, sz, vp]
+    L.attn_fwd_fp8qk.restype = i
+    L.attn_fwd_fp8qk_ex.argtypes = [vp, vp, vp, vp, i, vp, p64, i, i, i, i, f, vp, sz, vp]
+    L.attn_fwd_fp8qk_ex.restype = i
     L.attn_fwd_bf16_ex.argtypes = [vp, vp, vp, vp, i, vp, p64, i, i, i, i, f, vp]
     L.attn_fwd_bf16_ex.restype = i
     L.attn_fwd_int8qk_ex.argtypes = [vp, vp, vp, vp, i, vp, p64, i, i, i, i, f, vp, sz, vp]
@@ -224,10 +229,7 @@ def int8qk_views(workspace: torch.Tensor, B, H, S, D) -> dict:
             "k_codes": seg(4, torch.int8, (B, H, S, D))}
 
 
-def attn_fwd_int8qk(q, k, v, out=None, scale=None, workspace=None, *, out_dtype=None, lse=None):
-    """int8-QK attention (K smoothed by its channel mean, per-block int8 Q/K, bf16 PV).
-
-    Arguments and result as attn_fwd_bf16; lse is that of the quantized scores."""
+def _attn_q8(plain_fn, ex_fn, q, k, v, out, scale, workspace, out_dtype, lse):
     (B, H, S, D), out, lse_t, plain = _attn_args(q, k, v, out, out_dtype, lse)
     scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
     if workspace is None:
@@ -235,15 +237,30 @@ def attn_fwd_int8qk(q, k, v, out=None, scale=None, workspace=None, *, out_dtype=
     if workspace.dtype != torch.uint8 or not workspace.is_cuda or not workspace.is_contiguous():
         raise ValueError("workspace must be a contiguous uint8 CUDA tensor")
     if plain:
-        _check(lib().attn_fwd_int8qk(_ptr(q), _ptr(k), _ptr(v), _ptr(out), B, H, S, D, scale,
-                                     _ptr(workspace), workspace.numel(), _stream(q)))
+        _check(plain_fn(_ptr(q), _ptr(k), _ptr(v), _ptr(out), B, H, S, D, scale,
+                        _ptr(workspace), workspace.numel(), _stream(q)))
     else:
-        _check(lib().attn_fwd_int8qk_ex(
-            _ptr(q), _ptr(k), _ptr(v), _ptr(out),
-            OUT_BF16 if out.dtype == torch.bfloat16 else OUT_F32, _ptr(lse_t),
-            _strides_arg(q, k, v, out), B, H, S, D, scale, _ptr(workspace), workspace.numel(),
-            _stream(q)))
+        _check(ex_fn(_ptr(q), _ptr(k), _ptr(v), _ptr(out),
+                     OUT_BF16 if out.dtype == torch.bfloat16 else OUT_F32, _ptr(lse_t),
+                     _strides_arg(q, k, v, out), B, H, S, D, scale, _ptr(workspace),
+                     workspace.numel(), _stream(q)))
     return out if lse_t is None else (out, lse_t)
+
+
+def attn_fwd_int8qk(q, k, v, out=None, scale=None, workspace=None, *, out_dtype=None, lse=None):
+    """int8-QK attention (K smoothed by its channel mean, per-block int8 Q/K, bf16 PV).
+
+    Arguments and result as attn_fwd_bf16; lse is that of the quantized scores."""
+    return _attn_q8(lib().attn_fwd_int8qk, lib().attn_fwd_int8qk_ex, q, k, v, out, scale,
+                    workspace, out_dtype, lse)
+
+
+def attn_fwd_fp8qk(q, k, v, out=None, scale=None, workspace=None, *, out_dtype=None, lse=None):
+    """fp8-QK attention: as attn_fwd_int8qk with e4m3 codes (scale = amax / 448) and QK on the
+    fp8 matrix cores.  The workspace is the int8 call's (int8qk_workspace); its code views hold
+    e4m3 bytes."""
+    return _attn_q8(lib().attn_fwd_fp8qk, lib().attn_fwd_fp8qk_ex, q, k, v, out, scale,
+                    workspace, out_dtype, lse)
 
 
 def rel_l1_workspace_bytes(n: int) -> int:
@@ -274,18 +291,25 @@ def quant_probe_workspace_bytes(B, H, S, D, n_rows) -> int:
 
 
 def quant_probe_views(workspace, B, H, S, D, n_rows) -> dict:
-    """Views of the probe workspace: the chunk outputs `part` [ns, B, H, n_rows, D], their
-    log-sum-exps `lse` [ns, B, H, n_rows] and the key range [start, stop) of each chunk."""
+    """Views of the probe workspace: the chunk outputs `part` [B, ns + 1, H, n_rows, D], their
+    log-sum-exps `lse` [B, ns + 1, H, n_rows] and the key range [start, stop) of each chunk
+    that holds keys (`chunks`; the last slot is used only when ns L < S)."""
     ns = int(lib().attn_quant_probe_splits(B, H, S, D, n_rows))
     if ns == 0:
         raise DitAttnError(-1, "invalid shape or n_rows")
+    L = (S // ns) // 64 * 64
+    if ns == 1 or L == 0:
+        L = S
     al = lambda x: (x + 255) // 256 * 256  # noqa: E731
-    n_part = ns * B * H * n_rows * D
-    part = workspace[:n_part * 4].view(torch.float32).view(ns, B, H, n_rows, D)
+    n_part = B * (ns + 1) * H * n_rows * D
+    part = workspace[:n_part * 4].view(torch.float32).view(B, ns + 1, H, n_rows, D)
     off = al(n_part * 4)
-    lse = workspace[off:off + ns * B * H * n_rows * 4].view(torch.float32).view(ns, B, H, n_rows)
-    L = (-(-S // ns) + 63) // 64 * 64
-    return {"part": part, "lse": lse, "chunks": [(c * L, min(S, (c + 1) * L)) for c in range(ns)]}
+    lse = workspace[off:off + B * (ns + 1) * H * n_rows * 4].view(torch.float32)
+    lse = lse.view(B, ns + 1, H, n_rows)
+    chunks = [(c * L, (c + 1) * L) for c in range(ns)]
+    if ns * L < S:
+        chunks.append((ns * L, S))
+    return {"part": part, "lse": lse, "chunks": chunks}
 
 
 def attn_quant_probe(q, k, v, o_q, n_rows=256, scale=None, err=None, workspace=None):

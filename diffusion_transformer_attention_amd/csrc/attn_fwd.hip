@@ -1,4 +1,5 @@
-// Non-causal multi-head attention forward for gfx950 (MI355X): bf16 and int8-QK variants.
+// Non-causal multi-head attention forward for gfx950 (MI355X): bf16, int8-QK and fp8-QK
+// variants.
 //
 // O = softmax(Q K^T * scale) V, computed blockwise on chip so the S x S score matrix never
 // reaches HBM (the IO-aware tiling of the "Flash Attention 2 for Z-Image S3-DiT" page, method
@@ -9,8 +10,8 @@
 // Work decomposition (one workgroup = 8 wavefronts = 256 query rows of one (b, h); one
 // workgroup per CU, i.e. two wavefronts per SIMD):
 //   * Each wavefront owns 32 query rows.  Its Q fragment stays in VGPRs for the whole pass
-//     as the B operand of S^T = K Q^T (v_mfma_f32_32x32x16_bf16, or v_mfma_i32_32x32x32_i8
-//     on the int8 codes).  Computing S^T puts one query per lane (lane % 32) in the result,
+//     as the B operand of S^T = K Q^T (v_mfma_f32_32x32x16_bf16, v_mfma_i32_32x32x32_i8 on
+//     int8 codes, or v_mfma_f32_32x32x64_f8f6f4 on fp8 e4m3 codes).  Computing S^T puts one query per lane (lane % 32) in the result,
 //     so a row's maximum and sum are in-lane reductions plus one exchange with lane ^ 32
 //     (v_permlane32_swap), and rescaling a row of the output is a per-lane scalar.
 //   * The P^T tile left in the accumulator registers is directly the B operand of
@@ -47,7 +48,9 @@ namespace ditattn {
 
 namespace {
 
-constexpr int kQBlock = 128;    // int8 Q quantization block (tokens)
+enum Kind { kBF16 = 0, kInt8 = 1, kFp8 = 2 };  // what Q and K hold
+
+constexpr int kQBlock = 128;    // int8 / fp8 Q quantization block (tokens)
 constexpr int kBK = 64;         // keys per tile (= int8 K block)
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
@@ -134,7 +137,7 @@ struct KArgs {
 // the design and a third wave slot could not hold a second workgroup, yet aiming for three
 // squeezes the kernel into 168 VGPRs and serialises its K fragment reads behind the products.
 // (At D = 128 the cap changes nothing but the instruction schedule, measurably for the worse.)
-template <int D, bool INT8, int NW>
+template <int D, int KIND, int NW>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, D == 64 ? 2 : 8)))
 void attn_fwd_kernel(const uint8_t* __restrict__ qp, const uint8_t* __restrict__ kp,
                      const uint8_t* __restrict__ vp, uint8_t* __restrict__ op,
@@ -142,6 +145,9 @@ void attn_fwd_kernel(const uint8_t* __restrict__ qp, const uint8_t* __restrict__
                      const float* __restrict__ k_scale, const KArgs a) {
   const int Sq = a.Sq, Sk = a.Sk, n_qt = a.n_qt;
   const float c = a.c;
+  constexpr bool INT8 = KIND != kBF16;  // one-byte Q/K codes (int8 or fp8)
+  constexpr bool I8 = KIND == kInt8;
+  constexpr bool F8 = KIND == kFp8;
   using T = Tile<D, INT8, NW>;
   constexpr int kThreads = T::NT;
   constexpr int kBQ = T::BQ;
@@ -291,14 +297,34 @@ void attn_fwd_kernel(const uint8_t* __restrict__ qp, const uint8_t* __restrict__
   i32x16 ibias;
 #pragma unroll
   for (int r = 0; r < 16; ++r) ibias[r] = (int)__builtin_bit_cast(uint32_t, kBiasF);
-  if constexpr (INT8) asm volatile("" : "+v"(ibias));  // an opaque VGPR tuple, not a splat
+  if constexpr (I8) asm volatile("" : "+v"(ibias));  // an opaque VGPR tuple, not a splat
 
   // S^T tile of one K buffer: register 16 kb2 + r of lane holds key 32 kb2 + 8 (r / 4) +
   // 4 hh + r % 4, query q.  The int8 variant holds kBiasF + the integer score.
   auto qk = [&](const uint8_t* kbuf, float (&s)[32]) {
 #pragma unroll
     for (int kb2 = 0; kb2 < 2; ++kb2) {
-      if constexpr (INT8) {
+      if constexpr (F8) {
+        // fp8 e4m3 codes, 64 of each row per product: a lane's two 16-byte fragments f and
+        // f + 1 (bytes [32f + 16hh, +16) and [32f + 32 + 16hh, +16) of its row) form one
+        // operand.  Which k a byte stands for does not matter as long as both operands use
+        // the same layout, and they do: both are the rows' own bytes at the same offsets.
+        f32x16 acc = f32x16{};
+#pragma unroll
+        for (int f = 0; f < T::NQF; f += 2) {
+          const u32x4 a0 = *reinterpret_cast<const u32x4*>(kbuf + kb2 * 32 * T::KROW + koffs[f]);
+          const u32x4 a1 = *reinterpret_cast<const u32x4*>(kbuf + kb2 * 32 * T::KROW + koffs[f + 1]);
+          const i32x8 a = {(int)a0[0], (int)a0[1], (int)a0[2], (int)a0[3],
+                           (int)a1[0], (int)a1[1], (int)a1[2], (int)a1[3]};
+          const i32x8 b = {(int)qf[f][0], (int)qf[f][1], (int)qf[f][2], (int)qf[f][3],
+                           (int)qf[f + 1][0], (int)qf[f + 1][1], (int)qf[f + 1][2], (int)qf[f + 1][3]};
+          // formats 0, 0: both operands e4m3; no block scales (the scales are applied with
+          // the softmax's exponent FMA)
+          acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, acc, 0, 0, 0, 0, 0, 0);
+        }
+#pragma unroll
+        for (int r = 0; r < 16; ++r) s[16 * kb2 + r] = acc[r];
+      } else if constexpr (I8) {
         // The accumulator starts at the bit pattern of kBiasF, so it ends as kBiasF + the
         // integer dot product, which read as fp32 is exactly that sum (see kBiasF)
         i32x16 acc;
@@ -359,7 +385,7 @@ void attn_fwd_kernel(const uint8_t* __restrict__ qp, const uint8_t* __restrict__
     if constexpr (INT8) cf = cq * k_scale[(size_t)bh * nkt + min(jt, nkt - 1)];
     // exponent offset: m_run, plus the bias carried by the int8 scores (cf * kBiasF, rounded
     // once; its error is far below the int8 quantization error of the scores themselves)
-    const float mb = INT8 ? fmaf(cf, kBiasF, m_run) : m_run;
+    const float mb = I8 ? fmaf(cf, kBiasF, m_run) : m_run;
 #pragma unroll
     for (int c4 = 0; c4 < 4; ++c4)
 #pragma unroll
@@ -385,7 +411,7 @@ void attn_fwd_kernel(const uint8_t* __restrict__ qp, const uint8_t* __restrict__
       cf = cq;
       if constexpr (INT8) cf = cq * k_scale[(size_t)bh * nkt + jt];
       float mx;
-      if constexpr (INT8) {
+      if constexpr (I8) {
         // biased int8 scores are positive floats (or -inf when masked): their bit patterns
         // order like signed integers
         int mi = __float_as_int(s[0]);
@@ -478,7 +504,7 @@ void attn_fwd_kernel(const uint8_t* __restrict__ qp, const uint8_t* __restrict__
   // 4-byte steps moved the long-video int8 call by up to 3% (shifts that are a multiple of 8
   // bytes from the unpadded placement were the slow ones) and the bf16 call by up to 1%.
   // These pads are the measured best for this loop and compiler.
-  pad_nops<INT8 ? 1 : 3>();
+  pad_nops<KIND == kInt8 ? 1 : 3>();
 
   // stage j reads S[j+1] and writes S[j+2]; consumes P[j] and produces P[j+1]
   int j = 0;
@@ -525,10 +551,10 @@ void attn_fwd_kernel(const uint8_t* __restrict__ qp, const uint8_t* __restrict__
   }
 }
 
-template <int D, bool INT8, int NW>
+template <int D, int KIND, int NW>
 hipError_t launch(const AttnCall& ac, const void* q, Strides qs, const void* k, Strides ks,
                   const float* q_scale, const float* k_scale, hipStream_t stream) {
-  using T = Tile<D, INT8, NW>;
+  using T = Tile<D, KIND != kBF16, NW>;
   KArgs a;
   a.qsb = qs.b; a.qsh = qs.h; a.qss = qs.s;
   a.ksb = ks.b; a.ksh = ks.h; a.kss = ks.s;
@@ -541,7 +567,7 @@ hipError_t launch(const AttnCall& ac, const void* q, Strides qs, const void* k, 
   a.c = ac.scale * kLog2e;
   a.o_bf16 = ac.o_bf16 ? 1 : 0;
   const long long nwg = (long long)ac.B * ac.H * a.n_qt;
-  hipLaunchKernelGGL((attn_fwd_kernel<D, INT8, NW>), dim3((unsigned)nwg), dim3(T::NT), 0, stream,
+  hipLaunchKernelGGL((attn_fwd_kernel<D, KIND, NW>), dim3((unsigned)nwg), dim3(T::NT), 0, stream,
                      static_cast<const uint8_t*>(q), static_cast<const uint8_t*>(k),
                      static_cast<const uint8_t*>(ac.v), static_cast<uint8_t*>(ac.o), ac.lse,
                      q_scale, k_scale, a);
@@ -557,8 +583,8 @@ constexpr int kWaves = 8;
 
 hipError_t launch_attn_bf16(const AttnCall& ac, hipStream_t stream) {
   if (ac.D == 64)
-    return launch<64, false, kWaves>(ac, ac.q, ac.qs, ac.k, ac.ks, nullptr, nullptr, stream);
-  return launch<128, false, kWaves>(ac, ac.q, ac.qs, ac.k, ac.ks, nullptr, nullptr, stream);
+    return launch<64, kBF16, kWaves>(ac, ac.q, ac.qs, ac.k, ac.ks, nullptr, nullptr, stream);
+  return launch<128, kBF16, kWaves>(ac, ac.q, ac.qs, ac.k, ac.ks, nullptr, nullptr, stream);
 }
 
 hipError_t launch_attn_int8(const AttnCall& ac, const int8_t* q_codes, const int8_t* k_codes,
@@ -566,8 +592,16 @@ hipError_t launch_attn_int8(const AttnCall& ac, const int8_t* q_codes, const int
   // the codes are the prepass's own contiguous [B, H, S, D] buffers
   const Strides cs{(int64_t)ac.H * ac.S * ac.D, (int64_t)ac.S * ac.D, ac.D};
   if (ac.D == 64)
-    return launch<64, true, kWaves>(ac, q_codes, cs, k_codes, cs, q_scale, k_scale, stream);
-  return launch<128, true, kWaves>(ac, q_codes, cs, k_codes, cs, q_scale, k_scale, stream);
+    return launch<64, kInt8, kWaves>(ac, q_codes, cs, k_codes, cs, q_scale, k_scale, stream);
+  return launch<128, kInt8, kWaves>(ac, q_codes, cs, k_codes, cs, q_scale, k_scale, stream);
+}
+
+hipError_t launch_attn_fp8(const AttnCall& ac, const uint8_t* q_codes, const uint8_t* k_codes,
+                           const float* q_scale, const float* k_scale, hipStream_t stream) {
+  const Strides cs{(int64_t)ac.H * ac.S * ac.D, (int64_t)ac.S * ac.D, ac.D};
+  if (ac.D == 64)
+    return launch<64, kFp8, kWaves>(ac, q_codes, cs, k_codes, cs, q_scale, k_scale, stream);
+  return launch<128, kFp8, kWaves>(ac, q_codes, cs, k_codes, cs, q_scale, k_scale, stream);
 }
 
 }  // namespace ditattn

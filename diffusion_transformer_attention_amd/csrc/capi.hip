@@ -92,9 +92,9 @@ void contiguous_strides(int H, int S, int D, int64_t st[12]) {
   }
 }
 
-// The int8 path after validation: workspace check, prepass, attention.
-int int8qk_run(const ditattn::AttnCall& ac, void* workspace, size_t workspace_bytes,
-               hipStream_t s) {
+// The int8 / fp8 path after validation: workspace check, prepass, attention.
+int q8_run(const ditattn::AttnCall& ac, bool fp8, void* workspace, size_t workspace_bytes,
+           hipStream_t s) {
   size_t off[6];
   const size_t need = attn_int8qk_workspace_offsets(ac.B, ac.H, ac.S, ac.D, off);
   if (!workspace || !aligned(workspace, kSegAlign) || workspace_bytes < need) return DITATTN_EWORKSPACE;
@@ -107,8 +107,12 @@ int int8qk_run(const ditattn::AttnCall& ac, void* workspace, size_t workspace_by
   double* partial = reinterpret_cast<double*>(ws + off[5]);
   const hipError_t e = ditattn::launch_prepass(ac.q, ac.qs, ac.k, ac.ks, k_mean, partial, q_codes,
                                                k_codes, q_scale, k_scale, ac.B, ac.H, ac.S, ac.D,
-                                               s);
+                                               fp8, s);
   if (e != hipSuccess) return DITATTN_EHIP;
+  if (fp8)
+    return status_of(ditattn::launch_attn_fp8(ac, reinterpret_cast<const uint8_t*>(q_codes),
+                                              reinterpret_cast<const uint8_t*>(k_codes), q_scale,
+                                              k_scale, s));
   return status_of(ditattn::launch_attn_int8(ac, q_codes, k_codes, q_scale, k_scale, s));
 }
 
@@ -191,8 +195,8 @@ int attn_fwd_int8qk(const void* q, const void* k, const void* v, float* o, int B
   if (st != DITATTN_OK) return st;
   int64_t strides[12];
   contiguous_strides(H, S, D, strides);
-  return int8qk_run(make_call(q, k, v, o, false, nullptr, strides, B, H, S, D, scale), workspace,
-                    workspace_bytes, static_cast<hipStream_t>(stream));
+  return q8_run(make_call(q, k, v, o, false, nullptr, strides, B, H, S, D, scale), false,
+                workspace, workspace_bytes, static_cast<hipStream_t>(stream));
 }
 
 int attn_fwd_int8qk_ex(const void* q, const void* k, const void* v, void* o, int out_dtype,
@@ -200,8 +204,28 @@ int attn_fwd_int8qk_ex(const void* q, const void* k, const void* v, void* o, int
                        float scale, void* workspace, size_t workspace_bytes, void* stream) {
   const int st = check_ex_args(q, k, v, o, out_dtype, lse, strides, B, H, S, D, scale);
   if (st != DITATTN_OK) return st;
-  return int8qk_run(
-      make_call(q, k, v, o, out_dtype == DITATTN_OUT_BF16, lse, strides, B, H, S, D, scale),
+  return q8_run(
+      make_call(q, k, v, o, out_dtype == DITATTN_OUT_BF16, lse, strides, B, H, S, D, scale), false,
+      workspace, workspace_bytes, static_cast<hipStream_t>(stream));
+}
+
+int attn_fwd_fp8qk(const void* q, const void* k, const void* v, float* o, int B, int H, int S,
+                   int D, float scale, void* workspace, size_t workspace_bytes, void* stream) {
+  const int st = check_attn_args(q, k, v, o, B, H, S, D, scale);
+  if (st != DITATTN_OK) return st;
+  int64_t strides[12];
+  contiguous_strides(H, S, D, strides);
+  return q8_run(make_call(q, k, v, o, false, nullptr, strides, B, H, S, D, scale), true,
+                workspace, workspace_bytes, static_cast<hipStream_t>(stream));
+}
+
+int attn_fwd_fp8qk_ex(const void* q, const void* k, const void* v, void* o, int out_dtype,
+                      float* lse, const int64_t* strides, int B, int H, int S, int D, float scale,
+                      void* workspace, size_t workspace_bytes, void* stream) {
+  const int st = check_ex_args(q, k, v, o, out_dtype, lse, strides, B, H, S, D, scale);
+  if (st != DITATTN_OK) return st;
+  return q8_run(
+      make_call(q, k, v, o, out_dtype == DITATTN_OUT_BF16, lse, strides, B, H, S, D, scale), true,
       workspace, workspace_bytes, static_cast<hipStream_t>(stream));
 }
 
@@ -222,16 +246,16 @@ int resid_rel_l1(const void* a, const void* b, int64_t n, float* out, void* work
 
 int attn_quant_probe_splits(int B, int H, int S, int D, int n_rows) {
   if (check_attn_shape(B, H, S, D) != DITATTN_OK || n_rows < 1 || n_rows > S) return 0;
-  return ditattn::probe_splits(B, H, S, n_rows);
+  return ditattn::probe_chunks(B, H, S, n_rows).ns;
 }
 
 size_t attn_quant_probe_workspace_bytes(int B, int H, int S, int D, int n_rows) {
   if (check_attn_shape(B, H, S, D) != DITATTN_OK || n_rows < 1 || n_rows > S) return 0;
-  const size_t ns = (size_t)ditattn::probe_splits(B, H, S, n_rows);
+  const size_t ns = (size_t)ditattn::probe_chunks(B, H, S, n_rows).ns + 1;  // + the tail
   const size_t rows = (size_t)B * H * n_rows;
   return align_up(ns * rows * D * sizeof(float), kSegAlign) +
          align_up(ns * rows * sizeof(float), kSegAlign) +
-         align_up((size_t)B * H * 2 * sizeof(double), kSegAlign);
+         align_up((size_t)B * H * ditattn::probe_row_groups(n_rows) * 2 * sizeof(double), kSegAlign);
 }
 
 int attn_quant_probe(const void* q, const void* k, const void* v, const void* o_q, int o_q_dtype,
@@ -244,7 +268,7 @@ int attn_quant_probe(const void* q, const void* k, const void* v, const void* o_
   if (strides[2] * (S / n_rows) >= (int64_t(1) << 24)) return DITATTN_EINVAL;
   const size_t need = attn_quant_probe_workspace_bytes(B, H, S, D, n_rows);
   if (!workspace || !aligned(workspace, kSegAlign) || workspace_bytes < need) return DITATTN_EWORKSPACE;
-  const size_t ns = (size_t)ditattn::probe_splits(B, H, S, n_rows);
+  const size_t ns = (size_t)ditattn::probe_chunks(B, H, S, n_rows).ns + 1;
   const size_t rows = (size_t)B * H * n_rows;
   uint8_t* ws = static_cast<uint8_t*>(workspace);
   float* part = reinterpret_cast<float*>(ws);

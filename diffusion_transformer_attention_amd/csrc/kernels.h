@@ -39,16 +39,21 @@ hipError_t launch_attn_bf16(const AttnCall& ac, hipStream_t stream);
 hipError_t launch_attn_int8(const AttnCall& ac, const int8_t* q_codes, const int8_t* k_codes,
                             const float* q_scale, const float* k_scale, hipStream_t stream);
 
+// The fp8-QK attention: as launch_attn_int8 with e4m3 codes (QK on the fp8 matrix cores).
+hipError_t launch_attn_fp8(const AttnCall& ac, const uint8_t* q_codes, const uint8_t* k_codes,
+                           const float* q_scale, const float* k_scale, hipStream_t stream);
+
 // Number of token chunks the K-mean partial pass splits each (b, h) into.
 int kmean_chunks(int B, int H, int S);
 
 // The int8 prepass: K channel mean (exact double-double sum, one division, one rounding to
 // fp32) and per-block int8 quantization of Q (128-token blocks) and of the mean-smoothed K
 // (64-token blocks).  Three launches: mean partial sums together with the Q blocks, the mean,
-// then the K blocks.  partial: scratch of B*H*kmean_chunks(B,H,S)*D double pairs.
+// then the K blocks.  partial: scratch of B*H*kmean_chunks(B,H,S)*D double pairs.  fp8: the
+// codes are fp8 e4m3 (scale = amax / 448, one rounding to e4m3) instead of int8.
 hipError_t launch_prepass(const void* q, Strides qs, const void* k, Strides ks, float* k_mean,
                           double* partial, int8_t* q_codes, int8_t* k_codes, float* q_scale,
-                          float* k_scale, int B, int H, int S, int D, hipStream_t stream);
+                          float* k_scale, int B, int H, int S, int D, bool fp8, hipStream_t stream);
 
 // Number of partial-sum workgroups the relative-L1 pass uses for n elements.
 int rel_l1_blocks(int64_t n);
@@ -65,11 +70,21 @@ hipError_t launch_fbcache_decide(const void* resid, const void* prev_resid, int6
 // Key chunks the quantization probe splits each (b, h) into for R sampled rows.
 int probe_splits(int B, int H, int S, int R);
 
+// The probe's chunks: ns chunks of L keys (L a multiple of 64, or L = S when ns = 1), then
+// `tail` = S - ns L remaining keys as chunk ns (none when tail = 0).
+struct ProbeChunks {
+  int ns, L, tail;
+};
+ProbeChunks probe_chunks(int B, int H, int S, int R);
+
+// Row groups of the probe's merge (its sums workspace holds B*H*groups double pairs).
+int probe_row_groups(int R);
+
 // The quantization probe: bf16 attention of R rows per (b, h), rows step/2 + i step with
-// step = S / R (q, k, v, scale and their strides from `base`), in probe_splits chunks of keys with their lse
-// into part (fp32 [ns][B*H][R][D]) and lse (fp32 [ns][B*H][R]); then err[1 + bh] (and err[0]
-// over all) = sqrt(sum |o_q - o|^2 / sum |o|^2) against the quantized output o_q on those rows.
-// sums: B*H double pairs.
+// step = S / R (q, k, v, scale and their strides from `base`), over the probe_chunks chunks of
+// keys, each with its lse: part fp32 [B][ns + 1][H][R][D], lse fp32 [B][ns + 1][H][R]; then
+// err[1 + bh] (and err[0] over all) = sqrt(sum |o_q - o|^2 / sum |o|^2) against the quantized
+// output o_q on those rows.  sums: B*H*probe_row_groups(R) double pairs.
 hipError_t launch_quant_probe(const AttnCall& base, const void* o_q, bool o_q_bf16, Strides oqs,
                               int R, float* err, float* part, float* lse, double* sums,
                               hipStream_t stream);

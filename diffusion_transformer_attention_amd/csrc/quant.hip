@@ -1,4 +1,5 @@
-// Prepass of the int8-QK attention for gfx950: K channel mean and per-block int8 codes.
+// Prepass of the int8-QK and fp8-QK attention for gfx950: K channel mean and per-block
+// 8-bit codes.
 //
 // 8-bit attention (SageAttention) is the backend the "TMAP image-to-video inference
 // acceleration" page adopts (section on combining with the quantized attention operator);
@@ -10,6 +11,9 @@
 //   Ks            = fp32(K) - k_mean                      (one fp32 subtraction)
 //   per block     amax = max |x|; scale = amax / 127 (IEEE fp32 division), 1.0 if amax == 0
 //   code          = clamp(rint(x / scale), -127, 127)    (IEEE division, ties to even)
+// fp8 e4m3 codes instead (QK on the fp8 matrix cores; the pages use fp8 for linear layers and
+// 8-bit attention): scale = amax / 448 (the largest finite e4m3 value), code = x / scale
+// clamped to [-448, 448] and rounded once to e4m3 (nearest, ties to even).
 // Q blocks are 128 tokens and K blocks 64 tokens of one (b, h); a tail block covers only the
 // valid tokens.  These kernels are bound by HBM bandwidth: every byte is read once (K twice:
 // once for the mean, once for the codes) and every code written once, with 16-byte accesses.
@@ -114,7 +118,7 @@ __global__ __launch_bounds__(kThreads) void kmean_final_kernel(const double* __r
 // ---- per-block quantization --------------------------------------------------------------
 // One block of BT tokens of (b, h) = (bh / H, bh % H): x is read through its strides, the
 // codes are written to the contiguous [B, H, S, D] buffer.
-template <int D, int BT, bool SMOOTH>
+template <int D, int BT, bool SMOOTH, bool FP8>
 __device__ __forceinline__ void quant_block(const uint16_t* __restrict__ x, Strides xs, int H,
                                             const float* __restrict__ mean,
                                             int8_t* __restrict__ codes, float* __restrict__ scale_out,
@@ -162,7 +166,8 @@ __device__ __forceinline__ void quant_block(const uint16_t* __restrict__ x, Stri
   if ((tid & 63) == 0) wmax[tid >> 6] = amax;
   __syncthreads();
   amax = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
-  const float scale = (amax == 0.f) ? 1.0f : amax / 127.0f;
+  // the largest code: 127 (int8) or 448 (the largest finite fp8 e4m3 value)
+  const float scale = (amax == 0.f) ? 1.0f : amax / (FP8 ? 448.0f : 127.0f);
   if (tid == 0) *scale_out = scale;
   // fl32(x / scale) is computed as fl32(fl64(x * fl64(1 / scale))), which is the same value
   // for every fp32 x and scale: the fp64 product is within 2^-52 (relative) of x / scale, while
@@ -177,11 +182,26 @@ __device__ __forceinline__ void quant_block(const uint16_t* __restrict__ x, Stri
     const int tok = id / CPR, ch = id % CPR;
     if (tok >= nt) continue;
     uint32_t packed[2] = {0u, 0u};
+    if constexpr (FP8) {
+      // x / scale (|x / scale| <= 448 up to one rounding, clamped), then one rounding to e4m3,
+      // nearest even (v_cvt_pk_fp8_f32); fp32 first is innocuous (24 >= 2 * 4 + 2 bits)
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      float qv = rintf((float)((double)v[r][e] * rinv));
-      qv = fminf(fmaxf(qv, -127.f), 127.f);
-      packed[e >> 2] |= ((uint32_t)(uint8_t)(int8_t)(int)qv) << (8 * (e & 3));
+      for (int w = 0; w < 2; ++w) {
+        float qv[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          qv[e] = fminf(fmaxf((float)((double)v[r][4 * w + e] * rinv), -448.f), 448.f);
+        int word = __builtin_amdgcn_cvt_pk_fp8_f32(qv[0], qv[1], 0, false);
+        word = __builtin_amdgcn_cvt_pk_fp8_f32(qv[2], qv[3], word, true);
+        packed[w] = (uint32_t)word;
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        float qv = rintf((float)((double)v[r][e] * rinv));
+        qv = fminf(fmaxf(qv, -127.f), 127.f);
+        packed[e >> 2] |= ((uint32_t)(uint8_t)(int8_t)(int)qv) << (8 * (e & 3));
+      }
     }
     *reinterpret_cast<u32x2*>(codes + base + (size_t)tok * D + ch * 8) = u32x2{packed[0], packed[1]};
   }
@@ -189,7 +209,7 @@ __device__ __forceinline__ void quant_block(const uint16_t* __restrict__ x, Stri
 
 // First pass of the prepass: the K-mean partial sums (ids below BH * nch) and, independent of
 // the mean, the Q blocks (the remaining ids) in one launch.
-template <int D>
+template <int D, bool FP8>
 __global__ __launch_bounds__(kThreads) void kmean_partial_quant_q_kernel(
     const uint16_t* __restrict__ q, Strides qs, const uint16_t* __restrict__ k, Strides ks, int H,
     double* __restrict__ partial, int8_t* __restrict__ q_codes, float* __restrict__ q_scale, int S,
@@ -200,13 +220,13 @@ __global__ __launch_bounds__(kThreads) void kmean_partial_quant_q_kernel(
   } else {
     const int j = id - BH * nch;
     const int bh = j / nqb, blk = j - bh * nqb;
-    quant_block<D, 128, false>(q, qs, H, nullptr, q_codes, q_scale + (size_t)bh * nqb + blk, S, bh,
+    quant_block<D, 128, false, FP8>(q, qs, H, nullptr, q_codes, q_scale + (size_t)bh * nqb + blk, S, bh,
                                blk);
   }
 }
 
 // Last pass: the K blocks, smoothed by the finished mean.
-template <int D>
+template <int D, bool FP8>
 __global__ __launch_bounds__(kThreads) void quant_k_kernel(const uint16_t* __restrict__ k,
                                                            Strides ks, int H,
                                                            const float* __restrict__ k_mean,
@@ -214,7 +234,7 @@ __global__ __launch_bounds__(kThreads) void quant_k_kernel(const uint16_t* __res
                                                            float* __restrict__ k_scale, int S,
                                                            int nkb) {
   const int bh = blockIdx.x / nkb, blk = blockIdx.x - bh * nkb;
-  quant_block<D, 64, true>(k, ks, H, k_mean, k_codes, k_scale + (size_t)bh * nkb + blk, S, bh, blk);
+  quant_block<D, 64, true, FP8>(k, ks, H, k_mean, k_codes, k_scale + (size_t)bh * nkb + blk, S, bh, blk);
 }
 
 }  // namespace
@@ -227,7 +247,7 @@ int kmean_chunks(int B, int H, int S) {
   return (int)(n < 1 ? 1 : n);
 }
 
-template <int D>
+template <int D, bool FP8>
 hipError_t launch_prepass_d(const uint16_t* q, Strides qs, const uint16_t* k, Strides ks,
                             float* k_mean, double* partial, int8_t* q_codes, int8_t* k_codes,
                             float* q_scale, float* k_scale, int B, int H, int S, hipStream_t stream) {
@@ -235,26 +255,33 @@ hipError_t launch_prepass_d(const uint16_t* q, Strides qs, const uint16_t* k, St
   const int nch = kmean_chunks(B, H, S);
   const int rows_per = (S + nch - 1) / nch;
   const int nqb = (S + 127) / 128, nkb = (S + 63) / 64;
-  hipLaunchKernelGGL(kmean_partial_quant_q_kernel<D>, dim3((unsigned)((long long)BH * (nch + nqb))),
-                     dim3(kThreads), 0, stream, q, qs, k, ks, H, partial, q_codes, q_scale, S, BH,
-                     nch, rows_per, nqb);
+  hipLaunchKernelGGL((kmean_partial_quant_q_kernel<D, FP8>),
+                     dim3((unsigned)((long long)BH * (nch + nqb))), dim3(kThreads), 0, stream, q, qs,
+                     k, ks, H, partial, q_codes, q_scale, S, BH, nch, rows_per, nqb);
   hipLaunchKernelGGL(kmean_final_kernel<D>, dim3((unsigned)BH), dim3(kThreads), 0, stream, partial,
                      k_mean, S, nch);
-  hipLaunchKernelGGL(quant_k_kernel<D>, dim3((unsigned)((long long)BH * nkb)), dim3(kThreads), 0,
-                     stream, k, ks, H, k_mean, k_codes, k_scale, S, nkb);
+  hipLaunchKernelGGL((quant_k_kernel<D, FP8>), dim3((unsigned)((long long)BH * nkb)), dim3(kThreads),
+                     0, stream, k, ks, H, k_mean, k_codes, k_scale, S, nkb);
   return hipGetLastError();
 }
 
 hipError_t launch_prepass(const void* q, Strides qs, const void* k, Strides ks, float* k_mean,
                           double* partial, int8_t* q_codes, int8_t* k_codes, float* q_scale,
-                          float* k_scale, int B, int H, int S, int D, hipStream_t stream) {
+                          float* k_scale, int B, int H, int S, int D, bool fp8, hipStream_t stream) {
   const auto* qq = static_cast<const uint16_t*>(q);
   const auto* kk = static_cast<const uint16_t*>(k);
-  if (D == 64)
-    return launch_prepass_d<64>(qq, qs, kk, ks, k_mean, partial, q_codes, k_codes, q_scale,
-                                k_scale, B, H, S, stream);
-  return launch_prepass_d<128>(qq, qs, kk, ks, k_mean, partial, q_codes, k_codes, q_scale,
-                               k_scale, B, H, S, stream);
+  if (D == 64) {
+    if (fp8)
+      return launch_prepass_d<64, true>(qq, qs, kk, ks, k_mean, partial, q_codes, k_codes, q_scale,
+                                        k_scale, B, H, S, stream);
+    return launch_prepass_d<64, false>(qq, qs, kk, ks, k_mean, partial, q_codes, k_codes, q_scale,
+                                       k_scale, B, H, S, stream);
+  }
+  if (fp8)
+    return launch_prepass_d<128, true>(qq, qs, kk, ks, k_mean, partial, q_codes, k_codes, q_scale,
+                                       k_scale, B, H, S, stream);
+  return launch_prepass_d<128, false>(qq, qs, kk, ks, k_mean, partial, q_codes, k_codes, q_scale,
+                                      k_scale, B, H, S, stream);
 }
 
 }  // namespace ditattn

@@ -104,6 +104,22 @@ DITATTN_API int attn_fwd_int8qk(const void* q, const void* k, const void* v, flo
                     int B, int H, int S, int D, float scale,
                     void* workspace, size_t workspace_bytes, void* stream);
 
+/* Attention with fp8 (OCP e4m3) Q and K and bf16 PV: the int8 call's steps with e4m3 codes.
+ * The pages run their linear layers in fp8 and their attention in 8 bits; CDNA4's fp8 matrix
+ * cores (v_mfma_f32_32x32x64_f8f6f4) run at the int8 rate, and a floating-point grid keeps
+ * small values of a block that holds an outlier.
+ *   arguments as attn_fwd_int8qk; the workspace has the same size and layout
+ *   (attn_int8qk_workspace_bytes / _offsets), its code segments holding e4m3 bytes
+ * Steps 1-2 as attn_fwd_int8qk; then per block amax = max|x|, scale = amax / 448 (IEEE fp32
+ * division; 448 is the largest finite e4m3 value), 1.0 if amax == 0;
+ * code = e4m3(clamp(x / scale, -448, 448)), x / scale an IEEE fp32 division, one rounding to
+ * e4m3 (nearest, ties to even; e4m3 has 3 fraction bits, exponent bias 7, subnormals below
+ * 2^-6).  s_ij = (sum_d qc_id kc_jd, products exact, fp32 accumulation) * q_scale * k_scale *
+ * scale; softmax and PV as attn_fwd_int8qk. */
+DITATTN_API int attn_fwd_fp8qk(const void* q, const void* k, const void* v, float* o,
+                   int B, int H, int S, int D, float scale,
+                   void* workspace, size_t workspace_bytes, void* stream);
+
 /* ---- extended attention calls: strided views, bf16 output, per-row log-sum-exp --------------
  *
  * Same operations as attn_fwd_bf16 / attn_fwd_int8qk, with three additions that the steps
@@ -141,6 +157,12 @@ DITATTN_API int attn_fwd_int8qk_ex(const void* q, const void* k, const void* v, 
                                    int B, int H, int S, int D, float scale,
                                    void* workspace, size_t workspace_bytes, void* stream);
 
+/* As attn_fwd_fp8qk with the additions above (lse of the fp8 scores). */
+DITATTN_API int attn_fwd_fp8qk_ex(const void* q, const void* k, const void* v, void* o,
+                                  int out_dtype, float* lse, const int64_t* strides,
+                                  int B, int H, int S, int D, float scale,
+                                  void* workspace, size_t workspace_bytes, void* stream);
+
 /* Workspace of resid_rel_l1, in bytes, for n elements (0 if n < 1). */
 DITATTN_API size_t resid_rel_l1_workspace_bytes(int64_t n);
 
@@ -165,15 +187,17 @@ DITATTN_API int resid_rel_l1(const void* a, const void* b, int64_t n, float* out
  * call's work.  Sampled row i = step / 2 + i * step with step = floor(S / n_rows): the middle
  * row of the i-th bin of step rows (integer division). */
 
-/* Number of key chunks ns the probe splits each (b, h) into (0 if the arguments are invalid):
- * enough to give the few sampled rows work for every CU. */
+/* Number of uniform key chunks ns the probe splits each (b, h) into (0 if the arguments are
+ * invalid): enough to give the few sampled rows work for every CU.  Chunk c < ns holds keys
+ * [c L, (c + 1) L) with L = 64 floor(floor(S / ns) / 64) (L = S when ns = 1); chunk ns holds
+ * the remaining keys [ns L, S), if any. */
 DITATTN_API int attn_quant_probe_splits(int B, int H, int S, int D, int n_rows);
 
 /* Workspace of attn_quant_probe, in bytes (0 if the shape or n_rows is invalid).  Layout, each
- * segment on a 256-byte boundary: fp32 [ns][B*H][n_rows][D] chunk outputs, fp32
- * [ns][B*H][n_rows] chunk log-sum-exps (chunk c holds keys [c L, min(S, (c+1) L)),
- * L = ceil(ceil(S / ns) / 64) * 64), fp64 [B*H][2] per-head sums.  After a call the chunk
- * segments hold the bf16 path's partial results for the sampled rows. */
+ * segment on a 256-byte boundary: fp32 [B][ns + 1][H][n_rows][D] chunk outputs, fp32
+ * [B][ns + 1][H][n_rows] chunk log-sum-exps, fp64 [B*H][ceil(n_rows / 8)][2] partial sums.  After a call the
+ * chunk segments hold the bf16 path's partial results for the sampled rows (chunk ns only if
+ * it has keys). */
 DITATTN_API size_t attn_quant_probe_workspace_bytes(int B, int H, int S, int D, int n_rows);
 
 /*   q, k, v, strides, B, H, S, D, scale : the quantized call's inputs, as in attn_fwd_bf16_ex

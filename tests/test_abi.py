@@ -32,9 +32,9 @@ def test_header_declares_the_three_calls():
     names = declared_functions()
     for n in ("attn_fwd_bf16", "attn_fwd_int8qk", "resid_rel_l1", "attn_fwd_bf16_ex",
               "attn_fwd_int8qk_ex", "fbcache_decide", "resid_add", "resid_sub",
-              "attn_quant_probe"):
+              "attn_quant_probe", "attn_fwd_fp8qk", "attn_fwd_fp8qk_ex"):
         assert n in names
-    assert len(names) == 15
+    assert len(names) == 17
 
 
 def test_library_exports_every_declared_symbol(L):
@@ -94,16 +94,18 @@ def test_bf16_argument_errors(L):
     assert _bf16(L, B=1 << 20, H=1 << 10, S=1 << 20) == EINVAL  # grid would overflow
 
 
-def test_int8_argument_errors(L):
+@pytest.mark.parametrize("name", ["attn_fwd_int8qk", "attn_fwd_fp8qk"])
+def test_int8_argument_errors(L, name):
+    fn = getattr(L, name)
     need = L.attn_int8qk_workspace_bytes(1, 1, 64, 64)
     args = [FAKE, FAKE + 0x1000, FAKE + 0x2000, FAKE + 0x3000, 1, 1, 64, 64, 0.125]
-    assert L.attn_fwd_int8qk(*args, None, need, None) == EWS
-    assert L.attn_fwd_int8qk(*args, FAKE + 0x8000, need - 1, None) == EWS
-    assert L.attn_fwd_int8qk(*args, FAKE + 0x8010, need, None) == EWS   # not 256-aligned
+    assert fn(*args, None, need, None) == EWS
+    assert fn(*args, FAKE + 0x8000, need - 1, None) == EWS
+    assert fn(*args, FAKE + 0x8010, need, None) == EWS   # not 256-aligned
     bad = list(args); bad[7] = 80
-    assert L.attn_fwd_int8qk(*bad, FAKE + 0x8000, need, None) == EUNSUP
+    assert fn(*bad, FAKE + 0x8000, need, None) == EUNSUP
     bad = list(args); bad[0] = None
-    assert L.attn_fwd_int8qk(*bad, FAKE + 0x8000, need, None) == EINVAL
+    assert fn(*bad, FAKE + 0x8000, need, None) == EINVAL
 
 
 def _contig(H, S, D):
@@ -111,48 +113,49 @@ def _contig(H, S, D):
 
 
 def _ex(L, strides=None, out_dtype=0, lse=None, q=FAKE, o=FAKE + 0x3000, B=1, H=2, S=64, D=64,
-        int8=False):
+        int8=False, fp8=False):
     st = _contig(H, S, D) if strides is None else strides
     arr = (ctypes.c_int64 * 12)(*st) if st is not False else None
     args = [q, FAKE + 0x1000, FAKE + 0x2000, o, out_dtype, lse, arr, B, H, S, D, 0.125]
     if int8:
         need = L.attn_int8qk_workspace_bytes(B, H, S, D)
-        return L.attn_fwd_int8qk_ex(*args, FAKE + 0x8000, need - 1, None)
+        fn = L.attn_fwd_fp8qk_ex if fp8 else L.attn_fwd_int8qk_ex
+        return fn(*args, FAKE + 0x8000, need - 1, None)
     return L.attn_fwd_bf16_ex(*args, None)
 
 
-@pytest.mark.parametrize("int8", [False, True])
-def test_ex_argument_errors(L, int8):
+@pytest.mark.parametrize("int8,fp8", [(False, False), (True, False), (True, True)])
+def test_ex_argument_errors(L, int8, fp8):
     # every bad call fails validation before anything is launched; the int8 calls get a too
     # small workspace, so a call that passed validation would return EWORKSPACE, not launch
     ok = EWS if int8 else None
-    assert _ex(L, strides=False, int8=int8) == EINVAL                     # NULL strides
+    assert _ex(L, strides=False, int8=int8, fp8=fp8) == EINVAL                     # NULL strides
     for bad in (-1, 2, 7):
-        assert _ex(L, out_dtype=bad, int8=int8) == EINVAL
-    assert _ex(L, q=None, int8=int8) == EINVAL
-    assert _ex(L, o=FAKE, int8=int8) == EINVAL                           # o aliases q
-    assert _ex(L, q=FAKE + 8, int8=int8) == EINVAL                       # misaligned
-    assert _ex(L, lse=FAKE + 0x3000, int8=int8) == EINVAL                # lse aliases o
-    assert _ex(L, lse=FAKE + 0x4002, int8=int8) == EINVAL                # lse misaligned
-    assert _ex(L, D=96, strides=_contig(2, 64, 96), int8=int8) == EUNSUP
+        assert _ex(L, out_dtype=bad, int8=int8, fp8=fp8) == EINVAL
+    assert _ex(L, q=None, int8=int8, fp8=fp8) == EINVAL
+    assert _ex(L, o=FAKE, int8=int8, fp8=fp8) == EINVAL                           # o aliases q
+    assert _ex(L, q=FAKE + 8, int8=int8, fp8=fp8) == EINVAL                       # misaligned
+    assert _ex(L, lse=FAKE + 0x3000, int8=int8, fp8=fp8) == EINVAL                # lse aliases o
+    assert _ex(L, lse=FAKE + 0x4002, int8=int8, fp8=fp8) == EINVAL                # lse misaligned
+    assert _ex(L, D=96, strides=_contig(2, 64, 96), int8=int8, fp8=fp8) == EUNSUP
     for t in range(4):
         for a in range(3):
             st = _contig(2, 64, 64); st[3 * t + a] = -64
-            assert _ex(L, strides=st, int8=int8) == EINVAL               # negative stride
+            assert _ex(L, strides=st, int8=int8, fp8=fp8) == EINVAL               # negative stride
             st = _contig(2, 64, 64); st[3 * t + a] += 2
-            assert _ex(L, strides=st, int8=int8) == EINVAL               # not 16-byte steps
+            assert _ex(L, strides=st, int8=int8, fp8=fp8) == EINVAL               # not 16-byte steps
     for t in range(3):
         st = _contig(2, 64, 64); st[3 * t + 2] = 1 << 24
-        assert _ex(L, strides=st, int8=int8) == EINVAL                   # token stride too big
+        assert _ex(L, strides=st, int8=int8, fp8=fp8) == EINVAL                   # token stride too big
     # fp32 output: strides in steps of 4 elements pass validation; bf16 output needs 8
     st = _contig(2, 64, 64); st[11] = 68
     if int8:
-        assert _ex(L, strides=st, int8=True) == ok
-        assert _ex(L, strides=st, out_dtype=1, int8=True) == EINVAL
+        assert _ex(L, strides=st, int8=True, fp8=fp8) == ok
+        assert _ex(L, strides=st, out_dtype=1, int8=True, fp8=fp8) == EINVAL
         # the output's token stride has no 2^24 limit; stride 0 (broadcast inputs) is valid
         st = _contig(2, 64, 64); st[11] = 1 << 30; st[0] = st[1] = 0
-        assert _ex(L, strides=st, int8=True) == ok
-        assert _ex(L, lse=FAKE + 0x4004, int8=True) == ok
+        assert _ex(L, strides=st, int8=True, fp8=fp8) == ok
+        assert _ex(L, lse=FAKE + 0x4004, int8=True, fp8=fp8) == ok
     else:
         assert _ex(L, strides=st, out_dtype=1) == EINVAL
 

@@ -1,0 +1,211 @@
+"""GPU parity of the fp8-QK attention (attn_fwd_fp8qk[_ex]) against the oracle.
+
+Bar (written here):
+  K mean, scales and e4m3 codes   bit-exact against oracle.quantize_qk_fp8
+  output                          rel-L2 <= 1e-2 against oracle.attention_fp8 on the same codes
+                                  (its deviation from exact attention is printed, not gated)
+  lse                             against oracle.log_sum_exp_fp8 within 2^-8 + S 2^-24 + 1e-4
+                                  (bf16 weights, fp32 sums, exp/log approximations) plus the fp32
+                                  accumulation of a score, D 2^-24 |q_codes| |k_codes| sq sk scale
+  strided views, bf16 output      bit-identical to the plain call
+"""
+import sys
+
+import numpy as np
+import pytest
+
+import datagen
+import oracle
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+if not torch.cuda.is_available():
+    pytest.skip("needs a GPU", allow_module_level=True)
+
+import diffusion_transformer_attention_amd as dta  # noqa: E402
+
+FP8_RELL2 = 1e-2
+BF16_MAXABS = 2e-2
+
+
+def announce(msg):
+    print(f"[gpu-fp8] {msg}", file=sys.stderr, flush=True)
+
+
+def dev(bits):
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).cuda()
+
+
+def f64(bits):
+    return datagen.bf16_to_f64(bits)
+
+
+def rel_l2(x, y):
+    return float(np.linalg.norm((x - y).ravel()) / np.linalg.norm(y.ravel()))
+
+
+def run_fp8(q, k, v, **kw):
+    B, H, S, D = q.shape
+    ws = dta.int8qk_workspace(B, H, S, D, "cuda")
+    res = dta.attn_fwd_fp8qk(dev(q), dev(k), dev(v), workspace=ws, **kw)
+    torch.cuda.synchronize()
+    views = {n: t.cpu().numpy() for n, t in dta.int8qk_views(ws, B, H, S, D).items()}
+    for n in ("q_codes", "k_codes"):
+        views[n] = views[n].view(np.uint8)
+    return res, views
+
+
+def check_quant_exact(views, ref, what):
+    for key in ("k_mean", "q_scale", "k_scale"):
+        g, r = views[key], ref[key]
+        mism = int(np.sum(g.view(np.uint32) != r.view(np.uint32)))
+        assert mism == 0, f"{what}: {key} differs in {mism} of {r.size} values"
+    for key in ("q_codes", "k_codes"):
+        bad = np.argwhere(views[key] != ref[key])
+        for i in bad[:8]:
+            i = tuple(int(x) for x in i)
+            announce(f"  {key}{list(i)}: gpu {views[key][i]:#04x} "
+                     f"({oracle.e4m3_value(np.array([views[key][i]]))[0]!r}), oracle {ref[key][i]:#04x} "
+                     f"({oracle.e4m3_value(np.array([ref[key][i]]))[0]!r})")
+        assert bad.shape[0] == 0, f"{what}: {key} differs in {bad.shape[0]} of {ref[key].size} values"
+    announce(f"{what}: K mean, scales and e4m3 codes bit-exact")
+
+
+def check_out(got, ref_q, ref_exact, what):
+    r = rel_l2(got, ref_q)
+    announce(f"{what}: rel-L2 vs fp8 oracle {r:.3e}; vs exact attention {rel_l2(got, ref_exact):.3e}")
+    assert np.all(np.isfinite(got)), what
+    assert r <= FP8_RELL2, (what, r)
+
+
+def oracle_out(q, k, v, ref, rows=None):
+    return oracle.attention_fp8(ref["q_codes"], ref["q_scale"], ref["k_codes"], ref["k_scale"],
+                                f64(v), rows=rows)
+
+
+def test_fp8_tiny_full():
+    announce("attn_fwd_fp8qk tiny B1 H2 S256 D64")
+    q, k, v = datagen.attention_inputs("tiny")
+    out, views = run_fp8(q, k, v)
+    ref = oracle.quantize_qk_fp8(f64(q), f64(k))
+    check_quant_exact(views, ref, "tiny")
+    check_out(out.cpu().numpy(), oracle_out(q, k, v, ref), oracle.attention(f64(q), f64(k), f64(v)), "tiny")
+
+
+@pytest.mark.parametrize("S,D", [(1, 64), (63, 128), (65, 64), (129, 128), (300, 128), (1000, 64)])
+def test_fp8_ragged_lengths(S, D):
+    announce(f"attn_fwd_fp8qk B2 H3 S{S} D{D}")
+    q = datagen.normal_bf16((2, 3, S, D), 800 + D, 0)
+    k = datagen.f64_to_bf16_bits(f64(datagen.normal_bf16((2, 3, S, D), 800 + D, 1)) + 1.5)
+    v = datagen.normal_bf16((2, 3, S, D), 800 + D, 2)
+    out, views = run_fp8(q, k, v)
+    ref = oracle.quantize_qk_fp8(f64(q), f64(k))
+    check_quant_exact(views, ref, f"S={S} D={D}")
+    check_out(out.cpu().numpy(), oracle_out(q, k, v, ref), oracle.attention(f64(q), f64(k), f64(v)),
+              f"S={S} D={D}")
+
+
+def test_fp8_outlier_blocks_and_tiny_values():
+    """Blocks holding one large outlier next to tiny values: the e4m3 grid keeps the small
+    values (subnormal codes included), and the codes stay bit-exact."""
+    S, D = 512, 128
+    announce(f"attn_fwd_fp8qk outliers B1 H2 S{S} D{D}")
+    rng = np.random.default_rng(77)
+    q = rng.standard_normal((1, 2, S, D)) * 0.01
+    k = rng.standard_normal((1, 2, S, D)) * 0.01
+    q[:, :, ::128, 5] = 30.0
+    k[:, :, ::64, 7] = -25.0
+    v = rng.standard_normal((1, 2, S, D))
+    q, k, v = (datagen.f64_to_bf16_bits(x) for x in (q, k, v))
+    out, views = run_fp8(q, k, v)
+    ref = oracle.quantize_qk_fp8(f64(q), f64(k))
+    check_quant_exact(views, ref, "outliers")
+    sub = np.sum((views["q_codes"] & 0x78) == 0) + np.sum((views["k_codes"] & 0x78) == 0)
+    announce(f"  {sub} codes in the subnormal range (incl. zero)")
+    assert sub > 0
+    check_out(out.cpu().numpy(), oracle_out(q, k, v, ref), oracle.attention(f64(q), f64(k), f64(v)), "outliers")
+
+
+def test_fp8_zero_scale_guard():
+    S, D = 1000, 128
+    q = datagen.normal_bf16((1, 2, S, D), 810, 0)
+    k = datagen.normal_bf16((1, 2, S, D), 810, 1)
+    v = datagen.normal_bf16((1, 2, S, D), 810, 2)
+    mean_v = f64(v).mean(axis=2, keepdims=True)
+    announce("attn_fwd_fp8qk guard: Q = 0 and identical K rows")
+    out, views = run_fp8(np.zeros_like(q), k, v)
+    assert np.all(views["q_scale"] == 1.0) and not views["q_codes"].any()
+    got = out.cpu().numpy()
+    assert np.abs(got - mean_v).max() <= BF16_MAXABS
+    kc = np.broadcast_to(k[:, :, 3:4], k.shape).copy()
+    out, views = run_fp8(q, kc, v)
+    assert np.all(views["k_scale"] == 1.0) and not views["k_codes"].any()
+    got = out.cpu().numpy()
+    assert np.abs(got - mean_v).max() <= BF16_MAXABS
+
+
+def test_fp8_image_full():
+    announce("attn_fwd_fp8qk image B1 H24 S4608 D128 (full oracle)")
+    q, k, v = datagen.attention_inputs("image")
+    out, views = run_fp8(q, k, v)
+    ref = oracle.quantize_qk_fp8(f64(q), f64(k))
+    check_quant_exact(views, ref, "image fp8")
+    check_out(out.cpu().numpy(), oracle_out(q, k, v, ref), oracle.attention(f64(q), f64(k), f64(v)), "image fp8")
+
+
+def test_fp8_longvideo_sampled():
+    q, k, v = datagen.attention_inputs("longvideo")
+    B, H, S, D = q.shape
+    rows = datagen.sample_rows(S, 128, seed=79)
+    announce(f"attn_fwd_fp8qk longvideo B{B} H{H} S{S} D{D}, {rows.size} sampled rows per head")
+    ws = dta.int8qk_workspace(B, H, S, D, "cuda")
+    out = dta.attn_fwd_fp8qk(dev(q), dev(k), dev(v), workspace=ws)
+    torch.cuda.synchronize()
+    got = out.index_select(2, torch.from_numpy(rows).cuda()).cpu().numpy()
+    views = {n: t.cpu().numpy() for n, t in dta.int8qk_views(ws, B, H, S, D).items()}
+    for n in ("q_codes", "k_codes"):
+        views[n] = views[n].view(np.uint8)
+    del out, ws
+    torch.cuda.empty_cache()
+    ref = oracle.quantize_qk_fp8(f64(q), f64(k))
+    check_quant_exact(views, ref, "longvideo fp8")
+    quant = np.empty_like(got, dtype=np.float64)
+    exact = np.empty_like(got, dtype=np.float64)
+    for h in range(H):
+        sl = (slice(0, 1), slice(h, h + 1))
+        quant[sl] = oracle.attention_fp8(ref["q_codes"][sl], ref["q_scale"][sl], ref["k_codes"][sl],
+                                         ref["k_scale"][sl], f64(v[sl]), rows=rows)
+        exact[sl] = oracle.attention_rows(f64(q[sl]), f64(k[sl]), f64(v[sl]), rows)
+    check_out(got, quant, exact, "longvideo fp8 (sampled rows)")
+
+
+@pytest.mark.parametrize("S,D", [(65, 64), (1000, 128)])
+def test_fp8_lse_and_views(S, D):
+    B, H = 1, 3
+    announce(f"attn_fwd_fp8qk_ex lse, strided views, bf16 output B{B} H{H} S{S} D{D}")
+    q = datagen.normal_bf16((B, H, S, D), 820 + D, 0)
+    k = datagen.f64_to_bf16_bits(f64(datagen.normal_bf16((B, H, S, D), 820 + D, 1)) + 0.5)
+    v = datagen.normal_bf16((B, H, S, D), 820 + D, 2)
+    (o, lse), views = run_fp8(q, k, v, lse=True)
+    ref = oracle.quantize_qk_fp8(f64(q), f64(k))
+    check_quant_exact(views, ref, "lse case")
+    want = oracle.log_sum_exp_fp8(views["q_codes"], views["q_scale"], views["k_codes"], views["k_scale"])
+    qv = oracle.e4m3_value(views["q_codes"])
+    kv = oracle.e4m3_value(views["k_codes"])
+    acc = D * 2.0 ** -24 * np.linalg.norm(qv, axis=-1).max() * np.linalg.norm(kv, axis=-1).max() \
+        * views["q_scale"].max() * views["k_scale"].max() / np.sqrt(D)
+    tol = 2.0 ** -8 + S * 2.0 ** -24 + 1e-4 + acc
+    err = np.abs(lse.cpu().numpy() - want).max()
+    announce(f"  lse max error {err:.3e} (bound {tol:.3e})")
+    assert err <= tol
+    # [B, S, H, D] views and a bf16 output give the same bits as the plain call
+    qd, kd, vd = dev(q), dev(k), dev(v)
+    plain = dta.attn_fwd_fp8qk(qd, kd, vd)
+    bshd = [t.permute(0, 2, 1, 3).contiguous().transpose(1, 2) for t in (qd, kd, vd)]
+    o1 = dta.attn_fwd_fp8qk(*bshd)
+    ob = dta.attn_fwd_fp8qk(qd, kd, vd, out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    assert torch.equal(o1.contiguous(), plain)
+    assert torch.equal(ob.view(torch.int16), plain.to(torch.bfloat16).view(torch.int16))
+    assert torch.equal(o, plain)

@@ -43,11 +43,12 @@ def f64(bits):
 
 
 def merged_rows(views):
-    part = views["part"].cpu().numpy().astype(np.float64)
-    lse = views["lse"].cpu().numpy().astype(np.float64)
-    m = lse.max(axis=0)
+    n = len(views["chunks"])
+    part = views["part"].cpu().numpy().astype(np.float64)[:, :n]   # [B, n, H, R, D]
+    lse = views["lse"].cpu().numpy().astype(np.float64)[:, :n]
+    m = lse.max(axis=1, keepdims=True)
     w = np.exp(lse - m)
-    return (w[..., None] * part).sum(axis=0) / w.sum(axis=0)[..., None]
+    return (w[..., None] * part).sum(axis=1) / w.sum(axis=1)[..., None]
 
 
 def rel_l2(x, y, axis=None):
@@ -111,7 +112,7 @@ def test_probe_against_host_and_oracle(B, H, S, D, R, layout, o8_bf16):
 
 
 def test_probe_longvideo_shape():
-    """The long-video shape with 256 rows per head: the chunked keys (ten chunks of ~11.9k)."""
+    """The long-video shape with 256 rows per head: ten chunks of 11840 keys and a tail."""
     B, H, S, D, R = 1, 24, 118800, 128, 256
     announce(f"attn_quant_probe longvideo B{B} H{H} S{S} D{D} rows {R}")
     q, k, v = datagen.attention_inputs("longvideo")
@@ -121,7 +122,7 @@ def test_probe_longvideo_shape():
     err = dta.attn_quant_probe(qd, kd, vd, o8, n_rows=R, workspace=ws)
     torch.cuda.synchronize()
     views = dta.quant_probe_views(ws, B, H, S, D, R)
-    assert len(views["chunks"]) == 10
+    assert len(views["chunks"]) == 11      # ten chunks of 11840 keys and a tail of 400
     rows = oracle.probe_rows(S, R)
     o16 = merged_rows(views)
     o8_rows = o8.cpu().numpy()[:, :, rows].astype(np.float64)
