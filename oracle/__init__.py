@@ -16,7 +16,8 @@ from .attention import attention, attention_rows, log_sum_exp
 from .quant import (k_channel_mean, smooth_k, quantize_blocks, quantize_qk,
                     attention_int8, dequantize_blocks, log_sum_exp_int8, probe_rows,
                     quant_probe_error, Q_BLOCK, K_BLOCK, QMAX, E4M3_MAX, e4m3_value, e4m3_round,
-                    quantize_blocks_fp8, quantize_qk_fp8, attention_fp8, log_sum_exp_fp8)
+                    quantize_blocks_fp8, quantize_qk_fp8, attention_fp8, log_sum_exp_fp8,
+                    quantize_v_fp8, attention_fp8_full)
 from .rel_l1 import rel_l1
 from .fbcache import (FBCacheConfig, FBCacheState, fbcache_decide, fbcache_run, bf16_round,
                       resid_add, resid_sub)
@@ -26,4 +27,4 @@ __all__ = ["attention", "attention_rows", "log_sum_exp", "log_sum_exp_int8", "k_
            "QMAX", "FBCacheConfig", "FBCacheState", "fbcache_decide", "fbcache_run", "bf16_round",
            "resid_add", "resid_sub", "probe_rows", "quant_probe_error", "E4M3_MAX", "e4m3_value",
            "e4m3_round", "quantize_blocks_fp8", "quantize_qk_fp8", "attention_fp8",
-           "log_sum_exp_fp8"]
+           "log_sum_exp_fp8", "quantize_v_fp8", "attention_fp8_full"]

@@ -285,3 +285,30 @@ def attention_fp8(q_codes, q_scale, k_codes, k_scale, v, scale: float | None = N
 def log_sum_exp_fp8(q_codes, q_scale, k_codes, k_scale, scale: float | None = None):
     """log sum_j exp(s_ij) of the fp8-path scores, fp64 [B, H, S]."""
     return log_sum_exp_int8(e4m3_value(q_codes), q_scale, e4m3_value(k_codes), k_scale, scale)
+
+
+# ---- fp8 for both products ---------------------------------------------------------------------
+#
+# The fp8 variant with V in e4m3 as well (PV on the fp8 matrix cores), this library's contract:
+#   V: one scale per (b, h, channel) over all S tokens, scale_v = amax / 448 (1.0 if amax == 0),
+#      code = e4m3(clamp(fl32(v / scale_v), -448, 448)), rounded once (as the Q / K codes).
+#   o_i = sum_j p_ij * vq_jd * scale_v[d] / sum_j p_ij  with p the exact softmax weights of the
+#      fp8 scores.  (The GPU rounds each weight to e4m3 at its running offset before the product;
+#      that rounding is not part of this definition: it perturbs every weight by at most 2^-4
+#      relative, and the parity tolerance covers it.)
+
+def quantize_v_fp8(v):
+    """Per-(b, h, channel) e4m3 codes of V: (codes uint8 [B, H, S, D], scales float32 [B, H, D])."""
+    x = np.asarray(v, dtype=np.float64).astype(np.float32)
+    amax = np.abs(x).max(axis=2)                                            # [B, H, D]
+    scale = np.where(amax == 0, np.float32(1.0), amax / np.float32(E4M3_MAX)).astype(np.float32)
+    q = np.clip(x / scale[:, :, None, :], np.float32(-E4M3_MAX), np.float32(E4M3_MAX))
+    return e4m3_round(q.astype(np.float64)), scale
+
+
+def attention_fp8_full(q_codes, q_scale, k_codes, k_scale, v_codes, v_scale,
+                       scale: float | None = None, rows=None):
+    """Attention with fp8 scores (as attention_fp8) and fp8 V: the exact softmax of the scores
+    applied to the dequantized V (codes times their channel scale), fp64."""
+    vq = e4m3_value(v_codes) * np.asarray(v_scale, dtype=np.float64)[:, :, None, :]
+    return attention_fp8(q_codes, q_scale, k_codes, k_scale, vq, scale, rows=rows)

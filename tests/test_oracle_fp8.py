@@ -128,3 +128,55 @@ def test_fp8_attention_reduces_to_exact_attention():
     np.testing.assert_allclose(got, oracle.attention(q, k, v, sc), rtol=1e-12, atol=1e-13)
     lse = oracle.log_sum_exp_fp8(qq["q_codes"], qq["q_scale"], qq["k_codes"], qq["k_scale"], sc)
     np.testing.assert_allclose(lse, oracle.log_sum_exp(q, k, sc), rtol=1e-12, atol=1e-12)
+
+
+def test_v_quantizer_per_channel_contract():
+    rng = np.random.default_rng(44)
+    v = rng.standard_normal((2, 3, 200, 16)) * np.linspace(0.1, 10, 16)
+    v[1, 2, :, 5] = 0.0                                     # an all-zero channel
+    codes, scales = oracle.quantize_v_fp8(v)
+    assert codes.shape == v.shape and scales.shape == (2, 3, 16)
+    assert scales[1, 2, 5] == 1.0 and not codes[1, 2, :, 5].any()
+    vals = oracle.e4m3_value(codes)
+    vf = v.astype(np.float32)
+    for b in range(2):
+        for h in range(3):
+            for d in range(16):
+                col = vf[b, h, :, d]
+                if not col.any():
+                    continue
+                amax = np.abs(col).max()
+                assert scales[b, h, d] == np.float32(amax) / np.float32(448)
+                assert np.abs(vals[b, h, :, d]).max() == 448.0          # the amax token
+                qv = (col / scales[b, h, d]).astype(np.float64)
+                bound = np.maximum(np.abs(qv) * 2.0 ** -4, 2.0 ** -10) * (1 + 1e-12)
+                assert np.all(np.abs(vals[b, h, :, d] - qv) <= bound)
+
+
+def test_full_fp8_attention_reduces_to_exact_attention():
+    # V on the e4m3 grid with 448 in every channel: scale 1, codes = values; with exact Q/K
+    # codes too (construction of the QK test above), the result is exact attention
+    rng = np.random.default_rng(45)
+    S, D = 256, 16
+    g = oracle.e4m3_value(np.arange(127, dtype=np.uint8))
+    def grid_values(shape):
+        return rng.choice(g[40:110], size=shape) * rng.choice([-1.0, 1.0], size=shape)
+    q = grid_values((1, 2, S, D))
+    q[:, :, ::128, 0] = 448.0
+    half = grid_values((1, 2, S // 2, D))
+    half[:, :, ::32, 1] = 448.0
+    k = np.concatenate([half, -half], axis=2)
+    v = grid_values((1, 2, S, D))
+    v[:, :, 7, :] = 448.0
+    qq = oracle.quantize_qk_fp8(q, k)
+    vc, vs = oracle.quantize_v_fp8(v)
+    assert np.all(vs == 1.0) and np.array_equal(oracle.e4m3_value(vc), v)
+    sc = 1 / 2048.0
+    got = oracle.attention_fp8_full(qq["q_codes"], qq["q_scale"], qq["k_codes"], qq["k_scale"],
+                                    vc, vs, sc)
+    np.testing.assert_allclose(got, oracle.attention(q, k, v, sc), rtol=1e-12, atol=1e-9)
+    # and a V scale that is not 1 is applied per channel
+    vc2, vs2 = oracle.quantize_v_fp8(v * 0.25)
+    got2 = oracle.attention_fp8_full(qq["q_codes"], qq["q_scale"], qq["k_codes"], qq["k_scale"],
+                                     vc2, vs2, sc)
+    np.testing.assert_allclose(got2, 0.25 * got, rtol=1e-12, atol=1e-9)
