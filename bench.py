@@ -167,9 +167,13 @@ def time_fbcache(torch, dta, stream, ev, a, b, iters=20):
     return res
 
 
-def time_fp8(torch, dta, stream, ev, q, k, v, o, ws, iters=3):
-    """fp8-QK attention on the long-video workload (whole call: mean, e4m3 codes, attention)."""
-    fn = lambda: dta.attn_fwd_fp8qk(q, k, v, out=o, workspace=ws)  # noqa: E731
+def time_fp8(torch, dta, stream, ev, q, k, v, o, ws, iters=3, both=False):
+    """fp8 attention on the long-video workload (whole call: mean, e4m3 codes, attention);
+    both: V in e4m3 too (attn_fwd_fp8), else fp8 QK only (attn_fwd_fp8qk)."""
+    if both:
+        fn = lambda: dta.attn_fwd_fp8(q, k, v, out=o, workspace=ws)  # noqa: E731
+    else:
+        fn = lambda: dta.attn_fwd_fp8qk(q, k, v, out=o, workspace=ws)  # noqa: E731
     fn()
     e0, e1 = ev(), ev()
     torch.cuda.synchronize()
@@ -182,7 +186,30 @@ def time_fp8(torch, dta, stream, ev, q, k, v, o, ws, iters=3):
     B, H, S, D = q.shape
     tops = attn_flops(B, H, S, D) / (ms * 1e-3) / 1e12
     return {"ms": ms, "tflops": tops, "frac_fp8_peak": tops / PEAK_INT8_TOPS,
-            "note": "whole call; QK on fp8 e4m3 MFMA, PV bf16"}
+            "note": "whole call; QK and PV on fp8 e4m3 MFMA" if both else
+                    "whole call; QK on fp8 e4m3 MFMA, PV bf16"}
+
+
+def time_extended(torch, dta, stream, ev, q, k, v, iters=2):
+    """The extended bf16 call on the long-video workload: q, k, v as [B, S, H, D] views, bf16
+    output in that layout and the per-row log-sum-exp (same flops as the plain call)."""
+    B, H, S, D = q.shape
+    qs, ks, vs = (t.permute(0, 2, 1, 3).contiguous().transpose(1, 2) for t in (q, k, v))
+    o = torch.empty((B, S, H, D), dtype=torch.bfloat16, device="cuda").transpose(1, 2)
+    lse = torch.empty((B, H, S), dtype=torch.float32, device="cuda")
+    fn = lambda: dta.attn_fwd_bf16(qs, ks, vs, out=o, lse=lse)  # noqa: E731
+    fn()
+    e0, e1 = ev(), ev()
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(iters):
+        fn()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / iters
+    del qs, ks, vs, o, lse
+    return {"ms": ms, "tflops": attn_flops(B, H, S, D) / (ms * 1e-3) / 1e12,
+            "note": "[B,S,H,D] q/k/v views, bf16 output, lse"}
 
 
 def time_probe(torch, dta, stream, ev, q, k, v, o_int8, n_rows=256, iters=10):
@@ -212,7 +239,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--headline-only", action="store_true",
                     help="skip the extra timings (S=4608 attention, First Block Cache calls, "
-                         "quantization probe, fp8-QK attention): "
+                         "quantization probe, fp8-QK attention, extended bf16 call): "
                          "profiling runs, one shape per kernel")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy three times (the "
@@ -300,6 +327,12 @@ def main():
     fbc = None if args.headline_only else time_fbcache(torch, dta, stream, ev, a, b)
     probe = None if args.headline_only else time_probe(torch, dta, stream, ev, q, k, v, o_int8)
     fp8 = None if args.headline_only else time_fp8(torch, dta, stream, ev, q, k, v, o_int8, ws8)
+    fp8_all = None
+    if not args.headline_only:
+        ws_f8 = dta.fp8_workspace(B, H, S, D, "cuda")
+        fp8_all = time_fp8(torch, dta, stream, ev, q, k, v, o_int8, ws_f8, both=True)
+        del ws_f8
+    ext = None if args.headline_only else time_extended(torch, dta, stream, ev, q, k, v)
 
     traffic = load_traffic()
     line = {
@@ -331,6 +364,8 @@ def main():
             "fbcache_118800x3072": fbc,
             "quant_probe": probe,
             "fp8qk": fp8,
+            "fp8_qk_pv": fp8_all,
+            "bf16_ex_bshd_bf16out_lse": ext,
             "wall_s_timed": wall,
         },
     }

@@ -11,6 +11,7 @@ Entry points (same names as the C ABI in include/ditattn.h):
   attn_fwd_bf16(q, k, v, out=None, scale=None) -> out
   attn_fwd_int8qk(q, k, v, out=None, scale=None, workspace=None) -> out
   attn_fwd_fp8qk(q, k, v, out=None, scale=None, workspace=None) -> out
+  attn_fwd_fp8(q, k, v, out=None, scale=None, workspace=None) -> out   (fp8 QK and PV, D = 128)
   resid_rel_l1(a, b, out=None, workspace=None) -> out (fp32 device scalar, shape [1])
   attn_quant_probe(q, k, v, o_q, n_rows=256, scale=None) -> err (fp32 [1 + B*H])
   fbcache_decide(resid, prev_resid, state, config, workspace=None) -> state
@@ -33,7 +34,8 @@ import os
 
 import torch  # loaded first: the library then binds to the HIP runtime torch already holds
 
-__all__ = ["attn_fwd_bf16", "attn_fwd_int8qk", "attn_fwd_fp8qk", "resid_rel_l1", "int8qk_workspace",
+__all__ = ["attn_fwd_bf16", "attn_fwd_int8qk", "attn_fwd_fp8qk", "attn_fwd_fp8", "fp8_workspace",
+           "fp8_views", "resid_rel_l1", "int8qk_workspace",
            "int8qk_views", "int8qk_workspace_bytes", "rel_l1_workspace_bytes", "fbcache_decide",
            "resid_add", "resid_sub", "FBCacheConfig", "fbcache_state", "fbcache_state_values",
            "attn_quant_probe", "quant_probe_workspace_bytes", "quant_probe_views",
@@ -83,6 +85,14 @@ def lib() -> ctypes.CDLL:
     L.attn_fwd_int8qk.argtypes = [vp, vp, vp, vp, i, i, i, i, f, vp, sz, vp]
     L.attn_fwd_int8qk.restype = i
     p64 = ctypes.POINTER(i64)
+    L.attn_fwd_fp8.argtypes = [vp, vp, vp, vp, i, i, i, i, f, vp, sz, vp]
+    L.attn_fwd_fp8.restype = i
+    L.attn_fwd_fp8_ex.argtypes = [vp, vp, vp, vp, i, vp, p64, i, i, i, i, f, vp, sz, vp]
+    L.attn_fwd_fp8_ex.restype = i
+    L.attn_fp8_workspace_bytes.argtypes = [i, i, i, i]
+    L.attn_fp8_workspace_bytes.restype = sz
+    L.attn_fp8_workspace_offsets.argtypes = [i, i, i, i, ctypes.POINTER(sz)]
+    L.attn_fp8_workspace_offsets.restype = sz
     L.attn_fwd_fp8qk.argtypes = [vp, vp, vp, vp, i, i, i, i, f, vp, sz, vp]
     L.attn_fwd_fp8qk.restype = i
     L.attn_fwd_fp8qk_ex.argtypes = [vp, vp, vp, vp, i, vp, p64, i, i, i, i, f, vp, sz, vp]
@@ -229,11 +239,11 @@ def int8qk_views(workspace: torch.Tensor, B, H, S, D) -> dict:
             "k_codes": seg(4, torch.int8, (B, H, S, D))}
 
 
-def _attn_q8(plain_fn, ex_fn, q, k, v, out, scale, workspace, out_dtype, lse):
+def _attn_q8(plain_fn, ex_fn, q, k, v, out, scale, workspace, out_dtype, lse, ws_fn=None):
     (B, H, S, D), out, lse_t, plain = _attn_args(q, k, v, out, out_dtype, lse)
     scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
     if workspace is None:
-        workspace = int8qk_workspace(B, H, S, D, q.device)
+        workspace = (ws_fn or int8qk_workspace)(B, H, S, D, q.device)
     if workspace.dtype != torch.uint8 or not workspace.is_cuda or not workspace.is_contiguous():
         raise ValueError("workspace must be a contiguous uint8 CUDA tensor")
     if plain:
@@ -261,6 +271,37 @@ def attn_fwd_fp8qk(q, k, v, out=None, scale=None, workspace=None, *, out_dtype=N
     e4m3 bytes."""
     return _attn_q8(lib().attn_fwd_fp8qk, lib().attn_fwd_fp8qk_ex, q, k, v, out, scale,
                     workspace, out_dtype, lse)
+
+
+def fp8_workspace(B, H, S, D, device) -> torch.Tensor:
+    """A uint8 device buffer large enough for attn_fwd_fp8 on this shape."""
+    n = int(lib().attn_fp8_workspace_bytes(B, H, S, D))
+    if n == 0:
+        raise DitAttnError(-1, "invalid shape")
+    return torch.empty(n, dtype=torch.uint8, device=device)
+
+
+def fp8_views(workspace: torch.Tensor, B, H, S, D) -> dict:
+    """Views of the attn_fwd_fp8 workspace: as int8qk_views (codes as uint8 e4m3 bytes) plus
+    v_scale [B, H, D] and v_codes [B, H, S, D]."""
+    off = (ctypes.c_size_t * 9)()
+    total = lib().attn_fp8_workspace_offsets(B, H, S, D, off)
+    if total == 0 or workspace.numel() < total:
+        raise DitAttnError(-3, "workspace too small for this shape")
+    views = int8qk_views(workspace, B, H, S, D)
+    views["q_codes"] = views["q_codes"].view(torch.uint8)
+    views["k_codes"] = views["k_codes"].view(torch.uint8)
+    views["v_scale"] = workspace[off[6]:off[6] + B * H * D * 4].view(torch.float32).view(B, H, D)
+    views["v_codes"] = workspace[off[7]:off[7] + B * H * S * D].view(B, H, S, D)
+    return views
+
+
+def attn_fwd_fp8(q, k, v, out=None, scale=None, workspace=None, *, out_dtype=None, lse=None):
+    """Attention with fp8 e4m3 codes for Q, K (per block) and V (per channel): both products on
+    the fp8 matrix cores (D = 128).  Arguments and result as attn_fwd_bf16; the workspace comes
+    from fp8_workspace."""
+    return _attn_q8(lib().attn_fwd_fp8, lib().attn_fwd_fp8_ex, q, k, v, out, scale, workspace,
+                    out_dtype, lse, ws_fn=fp8_workspace)
 
 
 def rel_l1_workspace_bytes(n: int) -> int:

@@ -48,13 +48,18 @@ namespace ditattn {
 
 namespace {
 
-enum Kind { kBF16 = 0, kInt8 = 1, kFp8 = 2 };  // what Q and K hold
+// What Q and K hold, and V: bf16, int8 or fp8 codes for Q and K; bf16 V, or for kFp8All
+// fp8 codes for V as well (PV on the fp8 matrix cores).
+enum Kind { kBF16 = 0, kInt8 = 1, kFp8 = 2, kFp8All = 3 };
 
 constexpr int kQBlock = 128;    // int8 / fp8 Q quantization block (tokens)
 constexpr int kBK = 64;         // keys per tile (= int8 K block)
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kLazyW = 256.0f;  // 2^8: largest weight (and lane weight sum) kept as it is
+// fp8 weights are formed 2^4 times larger (the small ones then fall in e4m3's normal range, not
+// its coarse subnormals), and kept while their lane sum is <= 2^8, so every one is <= 256 < 448.
+constexpr float kLog2WScale8 = 4.0f;
 // 1.5 * 2^23: every fp32 in [2^23, 2^24) is an integer and consecutive integers have
 // consecutive bit patterns, so bits(kBiasF) + n read as fp32 is kBiasF + n for |n| < 2^22.
 // An int8 score is at most 127 * 127 * 128 < 2^21 in magnitude, so the int8 QK product
@@ -64,8 +69,10 @@ constexpr float kBiasF = 12582912.0f;
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+typedef int i32x2 __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) i32x2 lds_i32x2;
 
-template <int D, bool INT8, int NW>
+template <int D, bool INT8, int NW, bool V8 = false>
 struct Tile {
   static constexpr int NT = 64 * NW;             // threads per workgroup
   static constexpr int BQ = 32 * NW;             // query rows per workgroup
@@ -73,7 +80,7 @@ struct Tile {
   static constexpr int KCH = KROW / 16;          // 16-byte chunks per K row
   static constexpr int KRPG = 16 / KCH;          // K rows per 256-byte bank period
   static constexpr int KBYTES = kBK * KROW;      // one K tile
-  static constexpr int VROW = 2 * D;             // bytes per V row
+  static constexpr int VROW = V8 ? D : 2 * D;    // bytes per V row
   static constexpr int VCH = VROW / 16;
   static constexpr int VBYTES = kBK * VROW;      // one V tile
   static constexpr int KLD = (KBYTES / 16 + NT - 1) / NT;  // 16-byte loads per thread per K tile
@@ -103,6 +110,14 @@ __device__ __forceinline__ int vswz(int row, int ch) {
   } else {
     return ch ^ ((row & 2) << 1);  // masks {0, 0, 4, 4}
   }
+}
+
+// Swizzled chunk of fp8 V row `row` (128-byte rows, D = 128).  The transposing byte reads
+// fetch 16 bytes of each of 8 rows per 16 lanes (rows 8 a + 4 h + 0..3, a = 0, 1, chunk pair
+// of one 32-channel block); XORing the chunk with 2 bit1(row) + 4 bit3(row) spreads each 32-lane
+// half over 16 distinct 16-byte bank groups.
+__device__ __forceinline__ int vswz8(int row, int ch) {
+  return ch ^ (2 * ((row >> 1) & 1) + 4 * ((row >> 3) & 1));
 }
 
 // An empty asm that the compiler must assume redefines x (a VGPR value).
@@ -142,13 +157,17 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, D ==
 void attn_fwd_kernel(const uint8_t* __restrict__ qp, const uint8_t* __restrict__ kp,
                      const uint8_t* __restrict__ vp, uint8_t* __restrict__ op,
                      float* __restrict__ lse, const float* __restrict__ q_scale,
-                     const float* __restrict__ k_scale, const KArgs a) {
+                     const float* __restrict__ k_scale, const float* __restrict__ v_scale,
+                     const KArgs a) {
   const int Sq = a.Sq, Sk = a.Sk, n_qt = a.n_qt;
   const float c = a.c;
   constexpr bool INT8 = KIND != kBF16;  // one-byte Q/K codes (int8 or fp8)
   constexpr bool I8 = KIND == kInt8;
-  constexpr bool F8 = KIND == kFp8;
-  using T = Tile<D, INT8, NW>;
+  constexpr bool F8 = KIND == kFp8 || KIND == kFp8All;
+  constexpr bool V8 = KIND == kFp8All;  // fp8 V codes, PV on the fp8 matrix cores
+  static_assert(!V8 || D == 128, "fp8 V is laid out for D = 128");
+  using T = Tile<D, INT8, NW, V8>;
+  constexpr int EBV = V8 ? 1 : 2;       // bytes per V element
   constexpr int kThreads = T::NT;
   constexpr int kBQ = T::BQ;
   constexpr int EB = INT8 ? 1 : 2;  // bytes per Q/K element
@@ -176,8 +195,8 @@ void attn_fwd_kernel(const uint8_t* __restrict__ qp, const uint8_t* __restrict__
 
   const int bb = bh / a.H, hd = bh - bb * a.H;
   const uint8_t* kh = kp + (bb * a.ksb + hd * a.ksh) * EB;   // first key row of this (b, h)
-  const uint8_t* vh = vp + (bb * a.vsb + hd * a.vsh) * 2;
-  const int64_t krs = a.kss * EB, vrs = a.vss * 2;            // bytes between key / value rows
+  const uint8_t* vh = vp + (bb * a.vsb + hd * a.vsh) * EBV;
+  const int64_t krs = a.kss * EB, vrs = a.vss * EBV;          // bytes between key / value rows
   const int nkt = (Sk + kBK - 1) / kBK;
 
   // ---- Q fragment: B operand; lane holds query q, bytes [32f + 16hh, +16) of its row -------
@@ -219,7 +238,7 @@ void attn_fwd_kernel(const uint8_t* __restrict__ qp, const uint8_t* __restrict__
   for (int r = 0; r < T::VLD; ++r) {
     const int p = r * kThreads + tid;
     const int key = p / T::VCH, pch = p % T::VCH;
-    vofl[r] = (uint32_t)(key * vrs) + vswz<D>(key, pch) * 16;
+    vofl[r] = (uint32_t)(key * vrs) + (V8 ? vswz8(key, pch) : vswz<D>(key, pch)) * 16;
   }
   // First row of tile kt: kt * kBK, except a ragged last tile, which starts at Sk - kBK
   // (Sk >= kBK whenever more than one tile exists).  Tiles of K and of V are each loaded once,
@@ -266,7 +285,8 @@ void attn_fwd_kernel(const uint8_t* __restrict__ qp, const uint8_t* __restrict__
     for (int r = 0; r < T::VLD; ++r) {
       const int p = r * kThreads + tid;
       const int key = p / T::VCH, pch = p % T::VCH;
-      const uint32_t off = (uint32_t)(min(key, Sk - 1) * vrs) + vswz<D>(key, pch) * 16;
+      const uint32_t off =
+          (uint32_t)(min(key, Sk - 1) * vrs) + (V8 ? vswz8(key, pch) : vswz<D>(key, pch)) * 16;
       __builtin_amdgcn_global_load_lds(vh + off, (lds_void*)(vdst + (r * kThreads + wave_u * 64) * 16), 16, 0, 0);
     }
   };
@@ -284,8 +304,21 @@ void attn_fwd_kernel(const uint8_t* __restrict__ qp, const uint8_t* __restrict__
   int voffs[T::NDB];
 #pragma unroll
   for (int db = 0; db < T::NDB; ++db) {
-    const int col = 32 * db + 16 * ((lane >> 4) & 1) + 4 * (gj & 3);
-    voffs[db] = vrow * T::VROW + vswz<D>(vrow, col >> 3) * 16 + (col & 7) * 2;
+    if constexpr (V8) {
+      // fp8 V via ds_read_b64_tr_b8: in each 16-lane group lane t receives byte t % 8 of the
+      // 8-byte rows addressed by lanes 2 m + t / 8 (m = 0..7).  Lanes 2m and 2m + 1 address
+      // key k_m at channels n0 .. n0 + 7 and n0 + 8 .. n0 + 15, so lane t gets channel n0 + t
+      // for the keys k_0..k_7: with n0 = 32 db + 16 (g % 2) and k_m = 16 i + 8 (m / 4) + 4 hh
+      // + m % 4 for read i = 0..3, the lane's 32 bytes are its channel's values at exactly the
+      // keys (and in the order) its 32 weights occupy in the P^T operand.
+      const int m = gj >> 1;
+      const int r0 = 8 * (m >> 2) + 4 * hh + (m & 3);
+      const int f = 2 * ((r0 >> 1) & 1) + 4 * ((r0 >> 3) & 1);
+      voffs[db] = r0 * T::VROW + (((2 * db) ^ f) + ((lane >> 4) & 1)) * 16 + 8 * (gj & 1);
+    } else {
+      const int col = 32 * db + 16 * ((lane >> 4) & 1) + 4 * (gj & 3);
+      voffs[db] = vrow * T::VROW + vswz<D>(vrow, col >> 3) * 16 + (col & 7) * 2;
+    }
   }
 
   f32x16 oacc[T::NDB];
@@ -386,19 +419,41 @@ void attn_fwd_kernel(const uint8_t* __restrict__ qp, const uint8_t* __restrict__
     // exponent offset: m_run, plus the bias carried by the int8 scores (cf * kBiasF, rounded
     // once; its error is far below the int8 quantization error of the scores themselves)
     const float mb = I8 ? fmaf(cf, kBiasF, m_run) : m_run;
+    if constexpr (V8) {
+      // fp8 weights (2^4 times the softmax weights, see kLog2WScale8), four to a dword in the
+      // order of s (the P^T operand's byte order), in pb[0] and pb[1]; the row sum adds the
+      // fp32 weights (each <= 2^8 < 448 when kept)
+      float w[32];
 #pragma unroll
-    for (int c4 = 0; c4 < 4; ++c4)
+      for (int e = 0; e < 32; ++e)
+        w[e] = __builtin_amdgcn_exp2f(fmaf(s[e], cf, kLog2WScale8 - mb));
+      lt = 0.f;
 #pragma unroll
-      for (int e = 0; e < 8; ++e)
-        pb[c4][e] = (__bf16)__builtin_amdgcn_exp2f(fmaf(s[8 * c4 + e], cf, -mb));
-    // row sum of the bf16 weights that enter PV, two at a time on the dot unit
-    const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
-    lt = 0.f;
+      for (int e = 0; e < 32; ++e) lt += w[e];
+      u32x4 pw[2];
 #pragma unroll
-    for (int c4 = 0; c4 < 4; ++c4)
+      for (int d = 0; d < 8; ++d) {
+        int word = __builtin_amdgcn_cvt_pk_fp8_f32(w[4 * d], w[4 * d + 1], 0, false);
+        word = __builtin_amdgcn_cvt_pk_fp8_f32(w[4 * d + 2], w[4 * d + 3], word, true);
+        pw[d >> 2][d & 3] = (uint32_t)word;
+      }
+      pb[0] = __builtin_bit_cast(bf16x8, pw[0]);
+      pb[1] = __builtin_bit_cast(bf16x8, pw[1]);
+    } else {
 #pragma unroll
-      for (int e = 0; e < 8; e += 2)
-        lt = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pb[c4][e], pb[c4][e + 1]}, ones, lt, false);
+      for (int c4 = 0; c4 < 4; ++c4)
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          pb[c4][e] = (__bf16)__builtin_amdgcn_exp2f(fmaf(s[8 * c4 + e], cf, -mb));
+      // row sum of the bf16 weights that enter PV, two at a time on the dot unit
+      const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+      lt = 0.f;
+#pragma unroll
+      for (int c4 = 0; c4 < 4; ++c4)
+#pragma unroll
+        for (int e = 0; e < 8; e += 2)
+          lt = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pb[c4][e], pb[c4][e + 1]}, ones, lt, false);
+    }
   };
 
   // The rare path: a lane's weight sum above kLazyW (or inf / NaN, e.g. on the first tile)
@@ -407,7 +462,7 @@ void attn_fwd_kernel(const uint8_t* __restrict__ qp, const uint8_t* __restrict__
   auto settle = [&](int jt, const float (&s)[32], bf16x8 (&pb)[4], float& lt)
                     __attribute__((always_inline)) {
     float cf;
-    if (__builtin_amdgcn_ballot_w64(!(lt <= kLazyW)) != 0) {
+    if (__builtin_amdgcn_ballot_w64(!(lt <= kLazyW)) != 0) {  // (V8: the sum of 2^4 w <= 2^8)
       cf = cq;
       if constexpr (INT8) cf = cq * k_scale[(size_t)bh * nkt + jt];
       float mx;
@@ -454,6 +509,24 @@ void attn_fwd_kernel(const uint8_t* __restrict__ qp, const uint8_t* __restrict__
     weights(j + 1, s1, p1, lt, cf);
 
     // O^T += V[j]^T P[j]: lane holds channels 32 db + 8 (r / 4) + 4 hh + r % 4, query q
+    if constexpr (V8) {
+      const u32x4 pw0 = __builtin_bit_cast(u32x4, p0[0]), pw1 = __builtin_bit_cast(u32x4, p0[1]);
+      const i32x8 pf = {(int)pw0[0], (int)pw0[1], (int)pw0[2], (int)pw0[3],
+                        (int)pw1[0], (int)pw1[1], (int)pw1[2], (int)pw1[3]};
+#pragma unroll
+      for (int db = 0; db < T::NDB; ++db) {
+        const uint8_t* base = vb_cur + voffs[db];
+        i32x8 va;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          // keys 16 i + ...: 16 rows further on per read
+          const i32x2 x = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)(base + 16 * i * T::VROW));
+          va[2 * i] = x[0];
+          va[2 * i + 1] = x[1];
+        }
+        oacc[db] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(va, pf, oacc[db], 0, 0, 0, 0, 0, 0);
+      }
+    } else {
 #pragma unroll
     for (int c4 = 0; c4 < 4; ++c4) {
 #pragma unroll
@@ -466,6 +539,7 @@ void attn_fwd_kernel(const uint8_t* __restrict__ qp, const uint8_t* __restrict__
         oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), p0[c4],
                                                            oacc[db], 0, 0, 0);
       }
+    }
     }
     if (j + 1 < nkt) settle(j + 1, s1, p1, lt);
     mask_tile(j + 2, s2);
@@ -521,6 +595,17 @@ void attn_fwd_kernel(const uint8_t* __restrict__ qp, const uint8_t* __restrict__
   // ---- epilogue: O = O_acc / l (fp32 or bf16), and optionally the row's log-sum-exp ------
   const float l_tot = xor32_sum(l_run);
   const float inv = 1.f / l_tot;
+  if constexpr (V8) {
+    // the V codes' channel scales: lane holds channels 32 db + 8 jj + 4 hh + 0..3
+#pragma unroll
+    for (int db = 0; db < T::NDB; ++db)
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        const f32x4 sv = *reinterpret_cast<const f32x4*>(v_scale + (size_t)bh * D + 32 * db + 8 * jj + 4 * hh);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) oacc[db][4 * jj + e] *= sv[e];
+      }
+  }
   if (q < Sq) {
     const int64_t orow = bb * a.osb + hd * a.osh + (int64_t)q * a.oss;  // element offset
     if (a.o_bf16) {
@@ -546,19 +631,22 @@ void attn_fwd_kernel(const uint8_t* __restrict__ qp, const uint8_t* __restrict__
         }
     }
     // log sum_j exp(scale * s_j) = (m + log2 l) * ln 2: the weights are 2^(scale log2e s - m)
+    // (times 2^4 for fp8 V)
     if (lse != nullptr && hh == 0)
-      lse[(int64_t)bh * Sq + q] = (m_run + __builtin_amdgcn_logf(l_tot)) * kLn2;
+      lse[(int64_t)bh * Sq + q] =
+          (m_run + __builtin_amdgcn_logf(l_tot) - (V8 ? kLog2WScale8 : 0.f)) * kLn2;
   }
 }
 
 template <int D, int KIND, int NW>
 hipError_t launch(const AttnCall& ac, const void* q, Strides qs, const void* k, Strides ks,
-                  const float* q_scale, const float* k_scale, hipStream_t stream) {
-  using T = Tile<D, KIND != kBF16, NW>;
+                  const void* v, Strides vs, const float* q_scale, const float* k_scale,
+                  const float* v_scale, hipStream_t stream) {
+  using T = Tile<D, KIND != kBF16, NW, KIND == kFp8All>;
   KArgs a;
   a.qsb = qs.b; a.qsh = qs.h; a.qss = qs.s;
   a.ksb = ks.b; a.ksh = ks.h; a.kss = ks.s;
-  a.vsb = ac.vs.b; a.vsh = ac.vs.h; a.vss = ac.vs.s;
+  a.vsb = vs.b; a.vsh = vs.h; a.vss = vs.s;
   a.osb = ac.os.b; a.osh = ac.os.h; a.oss = ac.os.s;
   a.H = ac.H;
   a.Sq = ac.Sq;
@@ -569,8 +657,8 @@ hipError_t launch(const AttnCall& ac, const void* q, Strides qs, const void* k, 
   const long long nwg = (long long)ac.B * ac.H * a.n_qt;
   hipLaunchKernelGGL((attn_fwd_kernel<D, KIND, NW>), dim3((unsigned)nwg), dim3(T::NT), 0, stream,
                      static_cast<const uint8_t*>(q), static_cast<const uint8_t*>(k),
-                     static_cast<const uint8_t*>(ac.v), static_cast<uint8_t*>(ac.o), ac.lse,
-                     q_scale, k_scale, a);
+                     static_cast<const uint8_t*>(v), static_cast<uint8_t*>(ac.o), ac.lse,
+                     q_scale, k_scale, v_scale, a);
   return hipGetLastError();
 }
 
@@ -583,8 +671,10 @@ constexpr int kWaves = 8;
 
 hipError_t launch_attn_bf16(const AttnCall& ac, hipStream_t stream) {
   if (ac.D == 64)
-    return launch<64, kBF16, kWaves>(ac, ac.q, ac.qs, ac.k, ac.ks, nullptr, nullptr, stream);
-  return launch<128, kBF16, kWaves>(ac, ac.q, ac.qs, ac.k, ac.ks, nullptr, nullptr, stream);
+    return launch<64, kBF16, kWaves>(ac, ac.q, ac.qs, ac.k, ac.ks, ac.v, ac.vs, nullptr, nullptr,
+                                     nullptr, stream);
+  return launch<128, kBF16, kWaves>(ac, ac.q, ac.qs, ac.k, ac.ks, ac.v, ac.vs, nullptr, nullptr,
+                                    nullptr, stream);
 }
 
 hipError_t launch_attn_int8(const AttnCall& ac, const int8_t* q_codes, const int8_t* k_codes,
@@ -592,16 +682,29 @@ hipError_t launch_attn_int8(const AttnCall& ac, const int8_t* q_codes, const int
   // the codes are the prepass's own contiguous [B, H, S, D] buffers
   const Strides cs{(int64_t)ac.H * ac.S * ac.D, (int64_t)ac.S * ac.D, ac.D};
   if (ac.D == 64)
-    return launch<64, kInt8, kWaves>(ac, q_codes, cs, k_codes, cs, q_scale, k_scale, stream);
-  return launch<128, kInt8, kWaves>(ac, q_codes, cs, k_codes, cs, q_scale, k_scale, stream);
+    return launch<64, kInt8, kWaves>(ac, q_codes, cs, k_codes, cs, ac.v, ac.vs, q_scale, k_scale,
+                                     nullptr, stream);
+  return launch<128, kInt8, kWaves>(ac, q_codes, cs, k_codes, cs, ac.v, ac.vs, q_scale, k_scale,
+                                    nullptr, stream);
 }
 
 hipError_t launch_attn_fp8(const AttnCall& ac, const uint8_t* q_codes, const uint8_t* k_codes,
                            const float* q_scale, const float* k_scale, hipStream_t stream) {
   const Strides cs{(int64_t)ac.H * ac.S * ac.D, (int64_t)ac.S * ac.D, ac.D};
   if (ac.D == 64)
-    return launch<64, kFp8, kWaves>(ac, q_codes, cs, k_codes, cs, q_scale, k_scale, stream);
-  return launch<128, kFp8, kWaves>(ac, q_codes, cs, k_codes, cs, q_scale, k_scale, stream);
+    return launch<64, kFp8, kWaves>(ac, q_codes, cs, k_codes, cs, ac.v, ac.vs, q_scale, k_scale,
+                                    nullptr, stream);
+  return launch<128, kFp8, kWaves>(ac, q_codes, cs, k_codes, cs, ac.v, ac.vs, q_scale, k_scale,
+                                   nullptr, stream);
+}
+
+hipError_t launch_attn_fp8_all(const AttnCall& ac, const uint8_t* q_codes, const uint8_t* k_codes,
+                               const uint8_t* v_codes, const float* q_scale, const float* k_scale,
+                               const float* v_scale, hipStream_t stream) {
+  if (ac.D != 128) return hipErrorInvalidValue;
+  const Strides cs{(int64_t)ac.H * ac.S * ac.D, (int64_t)ac.S * ac.D, ac.D};
+  return launch<128, kFp8All, kWaves>(ac, q_codes, cs, k_codes, cs, v_codes, cs, q_scale, k_scale,
+                                      v_scale, stream);
 }
 
 }  // namespace ditattn

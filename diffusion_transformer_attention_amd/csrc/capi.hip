@@ -92,11 +92,16 @@ void contiguous_strides(int H, int S, int D, int64_t st[12]) {
   }
 }
 
-// The int8 / fp8 path after validation: workspace check, prepass, attention.
-int q8_run(const ditattn::AttnCall& ac, bool fp8, void* workspace, size_t workspace_bytes,
+enum Q8Mode { kQ8Int8, kQ8Fp8Qk, kQ8Fp8All };
+
+// The int8 / fp8 paths after validation: workspace check, prepass, attention.
+int q8_run(const ditattn::AttnCall& ac, Q8Mode mode, void* workspace, size_t workspace_bytes,
            hipStream_t s) {
-  size_t off[6];
-  const size_t need = attn_int8qk_workspace_offsets(ac.B, ac.H, ac.S, ac.D, off);
+  if (mode == kQ8Fp8All && ac.D != 128) return DITATTN_EUNSUPPORTED;
+  const bool fp8 = mode != kQ8Int8;
+  size_t off[9];
+  const size_t need = mode == kQ8Fp8All ? attn_fp8_workspace_offsets(ac.B, ac.H, ac.S, ac.D, off)
+                                        : attn_int8qk_workspace_offsets(ac.B, ac.H, ac.S, ac.D, off);
   if (!workspace || !aligned(workspace, kSegAlign) || workspace_bytes < need) return DITATTN_EWORKSPACE;
   uint8_t* ws = static_cast<uint8_t*>(workspace);
   float* k_mean = reinterpret_cast<float*>(ws + off[0]);
@@ -109,6 +114,17 @@ int q8_run(const ditattn::AttnCall& ac, bool fp8, void* workspace, size_t worksp
                                                k_codes, q_scale, k_scale, ac.B, ac.H, ac.S, ac.D,
                                                fp8, s);
   if (e != hipSuccess) return DITATTN_EHIP;
+  if (mode == kQ8Fp8All) {
+    float* v_scale = reinterpret_cast<float*>(ws + off[6]);
+    uint8_t* v_codes = ws + off[7];
+    float* v_partial = reinterpret_cast<float*>(ws + off[8]);
+    const hipError_t ev = ditattn::launch_vquant(ac.v, ac.vs, v_scale, v_partial, v_codes, ac.B,
+                                                 ac.H, ac.S, ac.D, s);
+    if (ev != hipSuccess) return DITATTN_EHIP;
+    return status_of(ditattn::launch_attn_fp8_all(ac, reinterpret_cast<const uint8_t*>(q_codes),
+                                                  reinterpret_cast<const uint8_t*>(k_codes), v_codes,
+                                                  q_scale, k_scale, v_scale, s));
+  }
   if (fp8)
     return status_of(ditattn::launch_attn_fp8(ac, reinterpret_cast<const uint8_t*>(q_codes),
                                               reinterpret_cast<const uint8_t*>(k_codes), q_scale,
@@ -195,7 +211,7 @@ int attn_fwd_int8qk(const void* q, const void* k, const void* v, float* o, int B
   if (st != DITATTN_OK) return st;
   int64_t strides[12];
   contiguous_strides(H, S, D, strides);
-  return q8_run(make_call(q, k, v, o, false, nullptr, strides, B, H, S, D, scale), false,
+  return q8_run(make_call(q, k, v, o, false, nullptr, strides, B, H, S, D, scale), kQ8Int8,
                 workspace, workspace_bytes, static_cast<hipStream_t>(stream));
 }
 
@@ -205,7 +221,7 @@ int attn_fwd_int8qk_ex(const void* q, const void* k, const void* v, void* o, int
   const int st = check_ex_args(q, k, v, o, out_dtype, lse, strides, B, H, S, D, scale);
   if (st != DITATTN_OK) return st;
   return q8_run(
-      make_call(q, k, v, o, out_dtype == DITATTN_OUT_BF16, lse, strides, B, H, S, D, scale), false,
+      make_call(q, k, v, o, out_dtype == DITATTN_OUT_BF16, lse, strides, B, H, S, D, scale), kQ8Int8,
       workspace, workspace_bytes, static_cast<hipStream_t>(stream));
 }
 
@@ -215,7 +231,7 @@ int attn_fwd_fp8qk(const void* q, const void* k, const void* v, float* o, int B,
   if (st != DITATTN_OK) return st;
   int64_t strides[12];
   contiguous_strides(H, S, D, strides);
-  return q8_run(make_call(q, k, v, o, false, nullptr, strides, B, H, S, D, scale), true,
+  return q8_run(make_call(q, k, v, o, false, nullptr, strides, B, H, S, D, scale), kQ8Fp8Qk,
                 workspace, workspace_bytes, static_cast<hipStream_t>(stream));
 }
 
@@ -225,7 +241,51 @@ int attn_fwd_fp8qk_ex(const void* q, const void* k, const void* v, void* o, int 
   const int st = check_ex_args(q, k, v, o, out_dtype, lse, strides, B, H, S, D, scale);
   if (st != DITATTN_OK) return st;
   return q8_run(
-      make_call(q, k, v, o, out_dtype == DITATTN_OUT_BF16, lse, strides, B, H, S, D, scale), true,
+      make_call(q, k, v, o, out_dtype == DITATTN_OUT_BF16, lse, strides, B, H, S, D, scale), kQ8Fp8Qk,
+      workspace, workspace_bytes, static_cast<hipStream_t>(stream));
+}
+
+size_t attn_fp8_workspace_offsets(int B, int H, int S, int D, size_t offsets[9]) {
+  size_t off6[6];
+  const size_t base = attn_int8qk_workspace_offsets(B, H, S, D, off6);
+  if (base == 0) return 0;
+  const size_t bh = (size_t)B * (size_t)H;
+  const size_t sizes[3] = {
+      bh * D * sizeof(float),                                             // v_scale
+      bh * (size_t)S * D,                                                 // v_codes
+      bh * (size_t)ditattn::kmean_chunks(B, H, S) * D * sizeof(float),    // amax partials
+  };
+  size_t off = base;
+  if (offsets)
+    for (int i = 0; i < 6; ++i) offsets[i] = off6[i];
+  for (int i = 0; i < 3; ++i) {
+    if (offsets) offsets[6 + i] = off;
+    off = align_up(off + sizes[i], kSegAlign);
+  }
+  return off;
+}
+
+size_t attn_fp8_workspace_bytes(int B, int H, int S, int D) {
+  return attn_fp8_workspace_offsets(B, H, S, D, nullptr);
+}
+
+int attn_fwd_fp8(const void* q, const void* k, const void* v, float* o, int B, int H, int S, int D,
+                 float scale, void* workspace, size_t workspace_bytes, void* stream) {
+  const int st = check_attn_args(q, k, v, o, B, H, S, D, scale);
+  if (st != DITATTN_OK) return st;
+  int64_t strides[12];
+  contiguous_strides(H, S, D, strides);
+  return q8_run(make_call(q, k, v, o, false, nullptr, strides, B, H, S, D, scale), kQ8Fp8All,
+                workspace, workspace_bytes, static_cast<hipStream_t>(stream));
+}
+
+int attn_fwd_fp8_ex(const void* q, const void* k, const void* v, void* o, int out_dtype,
+                    float* lse, const int64_t* strides, int B, int H, int S, int D, float scale,
+                    void* workspace, size_t workspace_bytes, void* stream) {
+  const int st = check_ex_args(q, k, v, o, out_dtype, lse, strides, B, H, S, D, scale);
+  if (st != DITATTN_OK) return st;
+  return q8_run(
+      make_call(q, k, v, o, out_dtype == DITATTN_OUT_BF16, lse, strides, B, H, S, D, scale), kQ8Fp8All,
       workspace, workspace_bytes, static_cast<hipStream_t>(stream));
 }
 

@@ -43,6 +43,12 @@ hipError_t launch_attn_int8(const AttnCall& ac, const int8_t* q_codes, const int
 hipError_t launch_attn_fp8(const AttnCall& ac, const uint8_t* q_codes, const uint8_t* k_codes,
                            const float* q_scale, const float* k_scale, hipStream_t stream);
 
+// fp8 for both products (D = 128 only): e4m3 Q/K codes as launch_attn_fp8, V as e4m3 codes
+// (contiguous [B, H, S, D]) with one scale per (b, h, channel); PV on the fp8 matrix cores.
+hipError_t launch_attn_fp8_all(const AttnCall& ac, const uint8_t* q_codes, const uint8_t* k_codes,
+                               const uint8_t* v_codes, const float* q_scale, const float* k_scale,
+                               const float* v_scale, hipStream_t stream);
+
 // Number of token chunks the K-mean partial pass splits each (b, h) into.
 int kmean_chunks(int B, int H, int S);
 
@@ -54,6 +60,12 @@ int kmean_chunks(int B, int H, int S);
 hipError_t launch_prepass(const void* q, Strides qs, const void* k, Strides ks, float* k_mean,
                           double* partial, int8_t* q_codes, int8_t* k_codes, float* q_scale,
                           float* k_scale, int B, int H, int S, int D, bool fp8, hipStream_t stream);
+
+// fp8 V (D = 128): per-(b, h, channel) amax of |V| over the S tokens (partials of
+// kmean_chunks token chunks: B*H*chunks*D floats in `partial`), v_scale = amax / 448 (1.0 for a
+// zero channel), and e4m3 codes of V / v_scale into the contiguous [B, H, S, D] v_codes.
+hipError_t launch_vquant(const void* v, Strides vs, float* v_scale, float* partial,
+                         uint8_t* v_codes, int B, int H, int S, int D, hipStream_t stream);
 
 // Number of partial-sum workgroups the relative-L1 pass uses for n elements.
 int rel_l1_blocks(int64_t n);

@@ -237,7 +237,134 @@ __global__ __launch_bounds__(kThreads) void quant_k_kernel(const uint16_t* __res
   quant_block<D, 64, true, FP8>(k, ks, H, k_mean, k_codes, k_scale + (size_t)bh * nkb + blk, S, bh, blk);
 }
 
+// ---- fp8 V: per-channel amax over all tokens, then e4m3 codes ---------------------------
+// Partial channel maxima of |V| over one token chunk (id = bh * nch + chunk): D / 8 threads per
+// row read 16 bytes each, every max is exact, so chunking changes nothing.
+template <int D>
+__global__ __launch_bounds__(kThreads) void vmax_partial_kernel(const uint16_t* __restrict__ v,
+                                                                Strides vs, int H,
+                                                                float* __restrict__ partial, int S,
+                                                                int nch, int rows_per) {
+  constexpr int TPR = D / 8;
+  constexpr int RPP = kThreads / TPR;
+  __shared__ float red[kThreads][8];
+  const int id = blockIdx.x;
+  const int bh = id / nch, chunk = id - bh * nch;
+  const int tid = threadIdx.x;
+  const int cg = tid % TPR, rg = tid / TPR;
+  const int r0 = chunk * rows_per;
+  const int r1 = min(S, r0 + rows_per);
+  const uint16_t* vh = v + (bh / H) * vs.b + (bh % H) * vs.h;
+  float mx[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  constexpr int U = 8;
+  int row = r0 + rg;
+  auto take = [&](const u32x4& x) {
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      mx[2 * w] = fmaxf(mx[2 * w], fabsf(bf16lo(x[w])));
+      mx[2 * w + 1] = fmaxf(mx[2 * w + 1], fabsf(bf16hi(x[w])));
+    }
+  };
+  for (; row + (U - 1) * RPP < r1; row += U * RPP) {
+    u32x4 x[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      x[u] = *reinterpret_cast<const u32x4*>(vh + (int64_t)(row + u * RPP) * vs.s + cg * 8);
+#pragma unroll
+    for (int u = 0; u < U; ++u) take(x[u]);
+  }
+  for (; row < r1; row += RPP) take(*reinterpret_cast<const u32x4*>(vh + (int64_t)row * vs.s + cg * 8));
+#pragma unroll
+  for (int e = 0; e < 8; ++e) red[tid][e] = mx[e];
+  __syncthreads();
+  if (tid < D) {
+    const int g = tid / 8, e = tid % 8;
+    float m = 0.f;
+    for (int r = 0; r < RPP; ++r) m = fmaxf(m, red[r * TPR + g][e]);
+    partial[((size_t)bh * nch + chunk) * D + tid] = m;
+  }
+}
+
+// One workgroup per (b, h): the channel maxima over all chunks and the scales amax / 448.
+template <int D>
+__global__ __launch_bounds__(kThreads) void vscale_kernel(const float* __restrict__ partial,
+                                                          float* __restrict__ v_scale, int nch) {
+  const int bh = blockIdx.x;
+  for (int d = threadIdx.x; d < D; d += kThreads) {
+    float m = 0.f;
+    for (int c = 0; c < nch; ++c) m = fmaxf(m, partial[((size_t)bh * nch + c) * D + d]);
+    v_scale[(size_t)bh * D + d] = (m == 0.f) ? 1.0f : m / 448.0f;
+  }
+}
+
+// e4m3 codes of one block of 64 tokens of (b, h) = (bh / H, bh % H), contiguous output.
+template <int D>
+__global__ __launch_bounds__(kThreads) void quant_v_kernel(const uint16_t* __restrict__ v, Strides vs,
+                                                           int H, const float* __restrict__ v_scale,
+                                                           uint8_t* __restrict__ codes, int S,
+                                                           int nvb) {
+  constexpr int CPR = D / 8;
+  constexpr int BT = 64;
+  constexpr int NC = (BT * CPR) / kThreads;
+  static_assert(NC >= 1 && (BT * CPR) % kThreads == 0, "block shape");
+  const int bh = blockIdx.x / nvb, blk = blockIdx.x - bh * nvb;
+  const int tid = threadIdx.x;
+  const int t0 = blk * BT;
+  const int nt = min(BT, S - t0);
+  const uint16_t* vrow0 = v + (bh / H) * vs.b + (bh % H) * vs.h + (int64_t)t0 * vs.s;
+  const size_t base = ((size_t)bh * S + t0) * D;
+#pragma unroll
+  for (int r = 0; r < NC; ++r) {
+    const int id = tid + r * kThreads;
+    const int tok = id / CPR, ch = id % CPR;
+    if (tok >= nt) continue;
+    const u32x4 w = *reinterpret_cast<const u32x4*>(vrow0 + (int64_t)tok * vs.s + ch * 8);
+    const f32x4 s0 = *reinterpret_cast<const f32x4*>(v_scale + (size_t)bh * D + ch * 8);
+    const f32x4 s1 = *reinterpret_cast<const f32x4*>(v_scale + (size_t)bh * D + ch * 8 + 4);
+    float x[8], sc[8];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      x[2 * e] = bf16lo(w[e]);
+      x[2 * e + 1] = bf16hi(w[e]);
+      sc[e] = s0[e];
+      sc[4 + e] = s1[e];
+    }
+    uint32_t packed[2];
+#pragma unroll
+    for (int d2 = 0; d2 < 2; ++d2) {
+      float qv[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        // fl32(x / scale) as fl32(x * fl64(1 / scale)) (the same value, see quant_block)
+        const double rinv = 1.0 / (double)sc[4 * d2 + e];
+        qv[e] = fminf(fmaxf((float)((double)x[4 * d2 + e] * rinv), -448.f), 448.f);
+      }
+      int word = __builtin_amdgcn_cvt_pk_fp8_f32(qv[0], qv[1], 0, false);
+      word = __builtin_amdgcn_cvt_pk_fp8_f32(qv[2], qv[3], word, true);
+      packed[d2] = (uint32_t)word;
+    }
+    *reinterpret_cast<u32x2*>(codes + base + (size_t)tok * D + ch * 8) = u32x2{packed[0], packed[1]};
+  }
+}
+
 }  // namespace
+
+hipError_t launch_vquant(const void* v, Strides vs, float* v_scale, float* partial,
+                         uint8_t* v_codes, int B, int H, int S, int D, hipStream_t stream) {
+  if (D != 128) return hipErrorInvalidValue;
+  const int BH = B * H;
+  const int nch = kmean_chunks(B, H, S);
+  const int rows_per = (S + nch - 1) / nch;
+  const int nvb = (S + 63) / 64;
+  const auto* vv = static_cast<const uint16_t*>(v);
+  hipLaunchKernelGGL(vmax_partial_kernel<128>, dim3((unsigned)((long long)BH * nch)), dim3(kThreads),
+                     0, stream, vv, vs, H, partial, S, nch, rows_per);
+  hipLaunchKernelGGL(vscale_kernel<128>, dim3((unsigned)BH), dim3(kThreads), 0, stream, partial,
+                     v_scale, nch);
+  hipLaunchKernelGGL(quant_v_kernel<128>, dim3((unsigned)((long long)BH * nvb)), dim3(kThreads), 0,
+                     stream, vv, vs, H, v_scale, v_codes, S, nvb);
+  return hipGetLastError();
+}
 
 int kmean_chunks(int B, int H, int S) {
   const long long bh = (long long)B * H;

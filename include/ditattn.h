@@ -120,6 +120,24 @@ DITATTN_API int attn_fwd_fp8qk(const void* q, const void* k, const void* v, floa
                    int B, int H, int S, int D, float scale,
                    void* workspace, size_t workspace_bytes, void* stream);
 
+/* Attention with fp8 for both products (D = 128): Q and K as attn_fwd_fp8qk, and V as e4m3
+ * codes with one scale per (b, h, channel) over all S tokens, so PV runs on the fp8 matrix
+ * cores as well (about half the matrix-core time of the bf16 call).
+ *   arguments as attn_fwd_int8qk; D must be 128 (else DITATTN_EUNSUPPORTED)
+ *   workspace : >= attn_fp8_workspace_bytes(B, H, S, D) bytes, 256-byte aligned; segments
+ *               [0]-[5] as the int8 call's (codes e4m3), then
+ *               [6] v_scale fp32 [B, H, D]   amax over the tokens / 448 (1.0 for amax == 0)
+ *               [7] v_codes e4m3 [B, H, S, D]  e4m3(clamp(V / v_scale, -448, 448)), one rounding
+ *               [8] scratch (partial channel maxima)
+ * o[b,h,i,d] = sum_j p_ij vq[b,h,j,d] v_scale[b,h,d] / sum_j p_ij with p the softmax weights of
+ * the fp8 scores.  Each weight enters the product rounded to e4m3 at the kernel's running
+ * offset (at most 2^-4 relative; the row sum uses the fp32 weights). */
+DITATTN_API size_t attn_fp8_workspace_bytes(int B, int H, int S, int D);
+DITATTN_API size_t attn_fp8_workspace_offsets(int B, int H, int S, int D, size_t offsets[9]);
+DITATTN_API int attn_fwd_fp8(const void* q, const void* k, const void* v, float* o,
+                 int B, int H, int S, int D, float scale,
+                 void* workspace, size_t workspace_bytes, void* stream);
+
 /* ---- extended attention calls: strided views, bf16 output, per-row log-sum-exp --------------
  *
  * Same operations as attn_fwd_bf16 / attn_fwd_int8qk, with three additions that the steps
@@ -162,6 +180,12 @@ DITATTN_API int attn_fwd_fp8qk_ex(const void* q, const void* k, const void* v, v
                                   int out_dtype, float* lse, const int64_t* strides,
                                   int B, int H, int S, int D, float scale,
                                   void* workspace, size_t workspace_bytes, void* stream);
+
+/* As attn_fwd_fp8 with the additions above. */
+DITATTN_API int attn_fwd_fp8_ex(const void* q, const void* k, const void* v, void* o,
+                                int out_dtype, float* lse, const int64_t* strides,
+                                int B, int H, int S, int D, float scale,
+                                void* workspace, size_t workspace_bytes, void* stream);
 
 /* Workspace of resid_rel_l1, in bytes, for n elements (0 if n < 1). */
 DITATTN_API size_t resid_rel_l1_workspace_bytes(int64_t n);

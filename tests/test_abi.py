@@ -32,9 +32,10 @@ def test_header_declares_the_three_calls():
     names = declared_functions()
     for n in ("attn_fwd_bf16", "attn_fwd_int8qk", "resid_rel_l1", "attn_fwd_bf16_ex",
               "attn_fwd_int8qk_ex", "fbcache_decide", "resid_add", "resid_sub",
-              "attn_quant_probe", "attn_fwd_fp8qk", "attn_fwd_fp8qk_ex"):
+              "attn_quant_probe", "attn_fwd_fp8qk", "attn_fwd_fp8qk_ex", "attn_fwd_fp8",
+              "attn_fwd_fp8_ex"):
         assert n in names
-    assert len(names) == 17
+    assert len(names) == 21
 
 
 def test_library_exports_every_declared_symbol(L):
@@ -64,6 +65,33 @@ def test_int8_workspace_layout(L, B, H, S, D):
         assert off[i] == expect and off[i] % 256 == 0
         expect = _align(expect + sz)
     assert off[5] == expect and total > off[5] and total % 256 == 0
+
+
+@pytest.mark.parametrize("B,H,S,D", [(1, 2, 256, 128), (1, 24, 118800, 128), (3, 1, 1, 128)])
+def test_fp8_workspace_layout(L, B, H, S, D):
+    off6 = (ctypes.c_size_t * 6)()
+    base = L.attn_int8qk_workspace_offsets(B, H, S, D, off6)
+    off = (ctypes.c_size_t * 9)()
+    total = L.attn_fp8_workspace_offsets(B, H, S, D, off)
+    assert total == L.attn_fp8_workspace_bytes(B, H, S, D)
+    assert list(off)[:6] == list(off6) and off[6] == base
+    assert off[7] == _align(off[6] + B * H * D * 4)
+    assert off[8] == _align(off[7] + B * H * S * D)
+    assert total > off[8] and total % 256 == 0
+
+
+def test_fp8_all_argument_errors(L):
+    need = L.attn_fp8_workspace_bytes(1, 1, 64, 128)
+    args = [FAKE, FAKE + 0x1000, FAKE + 0x2000, FAKE + 0x3000, 1, 1, 64, 128, 0.125]
+    assert L.attn_fwd_fp8(*args, None, need, None) == EWS
+    assert L.attn_fwd_fp8(*args, FAKE + 0x8000, need - 1, None) == EWS
+    bad = list(args); bad[7] = 64                      # fp8 V is laid out for D = 128 only
+    assert L.attn_fwd_fp8(*bad, FAKE + 0x8000, 1 << 30, None) == EUNSUP
+    bad = list(args); bad[0] = None
+    assert L.attn_fwd_fp8(*bad, FAKE + 0x8000, need, None) == EINVAL
+    st = (ctypes.c_int64 * 12)(*_contig(1, 64, 128))
+    assert L.attn_fwd_fp8_ex(FAKE, FAKE + 0x1000, FAKE + 0x2000, FAKE + 0x3000, 5, None, st, 1, 1,
+                             64, 128, 0.125, FAKE + 0x8000, need, None) == EINVAL
 
 
 def test_invalid_shapes_give_zero_workspace(L):

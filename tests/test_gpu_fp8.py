@@ -1,4 +1,4 @@
-"""GPU parity of the fp8-QK attention (attn_fwd_fp8qk[_ex]) against the oracle.
+"""GPU parity of the fp8 attention calls (attn_fwd_fp8qk[_ex], attn_fwd_fp8[_ex]) against the oracle.
 
 Bar (written here):
   K mean, scales and e4m3 codes   bit-exact against oracle.quantize_qk_fp8
@@ -205,6 +205,177 @@ def test_fp8_lse_and_views(S, D):
     bshd = [t.permute(0, 2, 1, 3).contiguous().transpose(1, 2) for t in (qd, kd, vd)]
     o1 = dta.attn_fwd_fp8qk(*bshd)
     ob = dta.attn_fwd_fp8qk(qd, kd, vd, out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    assert torch.equal(o1.contiguous(), plain)
+    assert torch.equal(ob.view(torch.int16), plain.to(torch.bfloat16).view(torch.int16))
+    assert torch.equal(o, plain)
+
+
+# ---------------------------------------------------------------------------------------------
+# fp8 for both products (attn_fwd_fp8, D = 128)
+#   Q, K, V codes and scales   bit-exact against oracle.quantize_qk_fp8 / quantize_v_fp8
+#   output                     against oracle.attention_fp8_full (the exact softmax of the fp8
+#                              scores applied to the dequantized V) within an error model of the
+#                              one step that definition leaves out: each weight enters PV
+#                              rounded to e4m3 (formed 16x larger, so w~ = 16 p / max p).  A
+#                              normal e4m3 value carries an unbiased relative error of variance
+#                              2^-7 / 12 (3 fraction bits, values spread over a binade); a
+#                              subnormal one (w~ < 2^-6) an absolute error of variance
+#                              (2^-9)^2 / 12.  Independent over keys, the squared output error of
+#                              row i has the expectation
+#                                E_i = sum_j var(w~_ij) |v_j|^2 / (sum_j w~_ij)^2,
+#                              and the bar is |o - o*|_2 <= 2 sqrt(sum_i E_i) + 2e-3 |o*|_2
+#                              (the second term: the bf16-path-sized rounding of everything else)
+# ---------------------------------------------------------------------------------------------
+
+def fp8_pv_error_model(ref, vq, rows=None, scale=None):
+    """sum_i E_i (see above) over the given query rows of every (b, h)."""
+    qv = oracle.e4m3_value(ref["q_codes"])
+    kv = oracle.e4m3_value(ref["k_codes"])
+    B, H, S, D = qv.shape
+    scale = 1.0 / np.sqrt(D) if scale is None else scale
+    rows = np.arange(S) if rows is None else np.asarray(rows)
+    sq = np.asarray(ref["q_scale"], np.float64)[:, :, rows // oracle.Q_BLOCK]
+    sk = np.repeat(np.asarray(ref["k_scale"], np.float64), oracle.K_BLOCK, axis=2)[:, :, :S]
+    vn2 = (vq ** 2).sum(axis=-1)                                   # |v_j|^2, [B, H, S]
+    total = 0.0
+    for b in range(B):
+        for h in range(H):
+            kt = np.ascontiguousarray(kv[b, h].T)
+            for r0 in range(0, rows.size, 512):
+                r = rows[r0:r0 + 512]
+                sc = (qv[b, h, r] @ kt) * sq[b, h, r0:r0 + 512, None] * sk[b, h][None, :] * scale
+                w = 16.0 * np.exp(sc - sc.max(axis=1, keepdims=True))
+                var = np.where(w >= 2.0 ** -6, w * w * 2.0 ** -7 / 12, 2.0 ** -18 / 12)
+                total += float(((var * vn2[b, h][None, :]).sum(axis=1) / w.sum(axis=1) ** 2).sum())
+    return total
+
+
+def check_out_model(got, ref_q, ref_exact, model, what):
+    err = float(np.linalg.norm((got - ref_q).ravel()))
+    bound = 2.0 * np.sqrt(model) + 2e-3 * float(np.linalg.norm(ref_q.ravel()))
+    announce(f"{what}: |o - o*| {err:.3e} (bound {bound:.3e}, model sqrt {np.sqrt(model):.3e}); "
+             f"rel-L2 vs fp8 oracle {rel_l2(got, ref_q):.3e}, vs exact {rel_l2(got, ref_exact):.3e}")
+    assert np.all(np.isfinite(got)), what
+    assert err <= bound, (what, err, bound)
+
+def run_fp8_all(q, k, v, **kw):
+    B, H, S, D = q.shape
+    ws = dta.fp8_workspace(B, H, S, D, "cuda")
+    res = dta.attn_fwd_fp8(dev(q), dev(k), dev(v), workspace=ws, **kw)
+    torch.cuda.synchronize()
+    views = {n: t.cpu().numpy() for n, t in dta.fp8_views(ws, B, H, S, D).items()}
+    return res, views
+
+
+def check_all_exact(views, q, k, v, what):
+    ref = oracle.quantize_qk_fp8(f64(q), f64(k))
+    check_quant_exact(views, ref, what)
+    vc, vs = oracle.quantize_v_fp8(f64(v))
+    assert np.array_equal(views["v_scale"].view(np.uint32), vs.view(np.uint32)), what
+    bad = np.argwhere(views["v_codes"] != vc)
+    for i in bad[:8]:
+        i = tuple(int(x) for x in i)
+        announce(f"  v_codes{list(i)}: gpu {views['v_codes'][i]:#04x}, oracle {vc[i]:#04x}")
+    assert bad.shape[0] == 0, f"{what}: v_codes differ in {bad.shape[0]} values"
+    return ref, vc, vs
+
+
+def oracle_all(ref, vc, vs, rows=None):
+    return oracle.attention_fp8_full(ref["q_codes"], ref["q_scale"], ref["k_codes"], ref["k_scale"],
+                                     vc, vs, rows=rows)
+
+
+@pytest.mark.parametrize("S", [1, 63, 64, 129, 300, 1000])
+def test_fp8_all_ragged_lengths(S):
+    D = 128
+    announce(f"attn_fwd_fp8 B2 H3 S{S} D{D}")
+    q = datagen.normal_bf16((2, 3, S, D), 830, 0)
+    k = datagen.f64_to_bf16_bits(f64(datagen.normal_bf16((2, 3, S, D), 830, 1)) + 1.5)
+    v = datagen.normal_bf16((2, 3, S, D), 830, 2)
+    out, views = run_fp8_all(q, k, v)
+    ref, vc, vs = check_all_exact(views, q, k, v, f"S={S}")
+    vq = oracle.e4m3_value(vc) * vs[:, :, None, :]
+    check_out_model(out.cpu().numpy(), oracle_all(ref, vc, vs), oracle.attention(f64(q), f64(k), f64(v)),
+                    fp8_pv_error_model(ref, vq), f"fp8 all S={S}")
+
+
+def test_fp8_all_zero_v_channel_and_scales():
+    S, D = 500, 128
+    announce(f"attn_fwd_fp8 zero V channel, channel scales B1 H2 S{S} D{D}")
+    q = datagen.normal_bf16((1, 2, S, D), 840, 0)
+    k = datagen.normal_bf16((1, 2, S, D), 840, 1)
+    v = f64(datagen.normal_bf16((1, 2, S, D), 840, 2)) * np.linspace(0.01, 20, D)
+    v[0, 1, :, 9] = 0.0
+    v = datagen.f64_to_bf16_bits(v)
+    out, views = run_fp8_all(q, k, v)
+    ref, vc, vs = check_all_exact(views, q, k, v, "channel scales")
+    assert views["v_scale"][0, 1, 9] == 1.0
+    got = out.cpu().numpy()
+    assert np.all(got[0, 1, :, 9] == 0.0)
+    vq = oracle.e4m3_value(vc) * vs[:, :, None, :]
+    check_out_model(got, oracle_all(ref, vc, vs), oracle.attention(f64(q), f64(k), f64(v)),
+                    fp8_pv_error_model(ref, vq), "channel scales")
+
+
+def test_fp8_all_image_full():
+    announce("attn_fwd_fp8 image B1 H24 S4608 D128 (full oracle)")
+    q, k, v = datagen.attention_inputs("image")
+    out, views = run_fp8_all(q, k, v)
+    ref, vc, vs = check_all_exact(views, q, k, v, "image fp8 all")
+    vq = oracle.e4m3_value(vc) * vs[:, :, None, :]
+    check_out_model(out.cpu().numpy(), oracle_all(ref, vc, vs), oracle.attention(f64(q), f64(k), f64(v)),
+                    fp8_pv_error_model(ref, vq), "image fp8 all")
+
+
+def test_fp8_all_longvideo_sampled():
+    q, k, v = datagen.attention_inputs("longvideo")
+    B, H, S, D = q.shape
+    rows = datagen.sample_rows(S, 128, seed=81)
+    announce(f"attn_fwd_fp8 longvideo B{B} H{H} S{S} D{D}, {rows.size} sampled rows per head")
+    ws = dta.fp8_workspace(B, H, S, D, "cuda")
+    out = dta.attn_fwd_fp8(dev(q), dev(k), dev(v), workspace=ws)
+    torch.cuda.synchronize()
+    got = out.index_select(2, torch.from_numpy(rows).cuda()).cpu().numpy()
+    views = {n: t.cpu().numpy() for n, t in dta.fp8_views(ws, B, H, S, D).items()}
+    del out, ws
+    torch.cuda.empty_cache()
+    ref, vc, vs = check_all_exact(views, q, k, v, "longvideo fp8 all")
+    quant = np.empty_like(got, dtype=np.float64)
+    exact = np.empty_like(got, dtype=np.float64)
+    for h in range(H):
+        sl = (slice(0, 1), slice(h, h + 1))
+        quant[sl] = oracle.attention_fp8_full(ref["q_codes"][sl], ref["q_scale"][sl],
+                                              ref["k_codes"][sl], ref["k_scale"][sl], vc[sl],
+                                              vs[sl], rows=rows)
+        exact[sl] = oracle.attention_rows(f64(q[sl]), f64(k[sl]), f64(v[sl]), rows)
+    vq = oracle.e4m3_value(vc) * vs[:, :, None, :]
+    check_out_model(got, quant, exact, fp8_pv_error_model(ref, vq, rows=rows),
+                    "longvideo fp8 all (sampled rows)")
+
+
+def test_fp8_all_lse_views_bf16():
+    B, H, S, D = 1, 3, 1000, 128
+    announce(f"attn_fwd_fp8_ex lse, strided views, bf16 output B{B} H{H} S{S} D{D}")
+    q = datagen.normal_bf16((B, H, S, D), 850, 0)
+    k = datagen.normal_bf16((B, H, S, D), 850, 1)
+    v = datagen.normal_bf16((B, H, S, D), 850, 2)
+    (o, lse), views = run_fp8_all(q, k, v, lse=True)
+    want = oracle.log_sum_exp_fp8(views["q_codes"], views["q_scale"], views["k_codes"], views["k_scale"])
+    qv = oracle.e4m3_value(views["q_codes"])
+    kv = oracle.e4m3_value(views["k_codes"])
+    acc = D * 2.0 ** -24 * np.linalg.norm(qv, axis=-1).max() * np.linalg.norm(kv, axis=-1).max() \
+        * views["q_scale"].max() * views["k_scale"].max() / np.sqrt(D)
+    # the row sum adds fp32 weights here (no bf16 rounding): 2^-8 still bounds it
+    tol = 2.0 ** -8 + S * 2.0 ** -24 + 1e-4 + acc
+    err = np.abs(lse.cpu().numpy() - want).max()
+    announce(f"  lse max error {err:.3e} (bound {tol:.3e})")
+    assert err <= tol
+    qd, kd, vd = dev(q), dev(k), dev(v)
+    plain = dta.attn_fwd_fp8(qd, kd, vd)
+    bshd = [t.permute(0, 2, 1, 3).contiguous().transpose(1, 2) for t in (qd, kd, vd)]
+    o1 = dta.attn_fwd_fp8(*bshd)
+    ob = dta.attn_fwd_fp8(qd, kd, vd, out_dtype=torch.bfloat16)
     torch.cuda.synchronize()
     assert torch.equal(o1.contiguous(), plain)
     assert torch.equal(ob.view(torch.int16), plain.to(torch.bfloat16).view(torch.int16))
