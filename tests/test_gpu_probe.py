@@ -44,8 +44,8 @@ def f64(bits):
 
 def merged_rows(views):
     n = len(views["chunks"])
-    part = views["part"].cpu().numpy().astype(np.float64)[:, :n]   # [B, n, H, R, D]
-    lse = views["lse"].cpu().numpy().astype(np.float64)[:, :n]
+    part = views["part"][:, :n].cpu().numpy().astype(np.float64)   # [B, n, H, R, D]
+    lse = views["lse"][:, :n].cpu().numpy().astype(np.float64)
     m = lse.max(axis=1, keepdims=True)
     w = np.exp(lse - m)
     return (w[..., None] * part).sum(axis=1) / w.sum(axis=1)[..., None]
