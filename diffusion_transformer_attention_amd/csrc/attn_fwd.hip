@@ -210,6 +210,16 @@ void attn_fwd_kernel(const uint8_t* __restrict__ qp, const uint8_t* __restrict__
       qf[f] = (q < Sq) ? x : u32x4{0u, 0u, 0u, 0u};
     }
   }
+  // fp8 V: the A operand of the weight-sum product.  In a 16x16x128 fp8 product the bytes of
+  // lane l are row l % 16 of A, or column l % 16 of B, over the same k group l / 16, and lane l
+  // receives result rows 4 (l / 16) .. +3 of column l % 16.  Row m takes k group m / 4 alone
+  // (e4m3 1.0, 0x38, where l / 16 == (l % 16) / 4, else 0), so result (m, n) is the byte sum
+  // of B lane 16 (m / 4) + n: for every lane, its own bytes.
+  i32x8 rsel = {};
+  if constexpr (V8) {
+    const int one = ((lane >> 4) & 3) == ((lane >> 2) & 3) ? 0x38383838 : 0;
+    rsel = i32x8{one, one, one, one, one, one, one, one};
+  }
   float cq = c;
   if constexpr (INT8) {
     const int nqb = (Sq + kQBlock - 1) / kQBlock;  // (the int8 path never samples: Sq = Sk)
@@ -421,24 +431,31 @@ void attn_fwd_kernel(const uint8_t* __restrict__ qp, const uint8_t* __restrict__
     const float mb = I8 ? fmaf(cf, kBiasF, m_run) : m_run;
     if constexpr (V8) {
       // fp8 weights (2^4 times the softmax weights, see kLog2WScale8), four to a dword in the
-      // order of s (the P^T operand's byte order), in pb[0] and pb[1]; the row sum adds the
-      // fp32 weights (each <= 2^8 < 448 when kept)
+      // order of s (the P^T operand's byte order), in pb[0] and pb[1]
       float w[32];
 #pragma unroll
       for (int e = 0; e < 32; ++e)
         w[e] = __builtin_amdgcn_exp2f(fmaf(s[e], cf, kLog2WScale8 - mb));
-      lt = 0.f;
-#pragma unroll
-      for (int e = 0; e < 32; ++e) lt += w[e];
       u32x4 pw[2];
 #pragma unroll
       for (int d = 0; d < 8; ++d) {
-        int word = __builtin_amdgcn_cvt_pk_fp8_f32(w[4 * d], w[4 * d + 1], 0, false);
+        // (both halves of the word are written: the first conversion's "old" word is any
+        // register, here its own source, so that no zero has to be materialised)
+        int word = __builtin_amdgcn_cvt_pk_fp8_f32(w[4 * d], w[4 * d + 1], __float_as_int(w[4 * d]), false);
         word = __builtin_amdgcn_cvt_pk_fp8_f32(w[4 * d + 2], w[4 * d + 3], word, true);
         pw[d >> 2][d & 3] = (uint32_t)word;
       }
       pb[0] = __builtin_bit_cast(bf16x8, pw[0]);
       pb[1] = __builtin_bit_cast(bf16x8, pw[1]);
+      // This lane's sum of its 32 fp8 weights as they enter PV, on the matrix cores: the
+      // packed weights are the B operand of a 16x16x128 product whose A (rsel) gives output
+      // row m the k group m / 4 alone, so each output of lane l adds the 32 bytes of lane l
+      // itself, exactly (at most 2^8 per weight: far inside fp32).
+      const i32x8 pf = {(int)pw[0][0], (int)pw[0][1], (int)pw[0][2], (int)pw[0][3],
+                        (int)pw[1][0], (int)pw[1][1], (int)pw[1][2], (int)pw[1][3]};
+      const f32x4 rs = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+          rsel, pf, f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 0, 0, 0);
+      lt = rs[0];
     } else {
 #pragma unroll
       for (int c4 = 0; c4 < 4; ++c4)
