@@ -82,37 +82,50 @@ __device__ __forceinline__ void kmean_partial(const uint16_t* __restrict__ k, St
   }
 }
 
-// One workgroup per (b, h): 256 / D lanes per channel each merge every (256 / D)-th chunk,
-// then a fixed tree joins the lanes; the exact sum is divided by S in fp64 and rounded once.
+// D / 32 workgroups per (b, h), 32 channels each: 8 lanes per channel each merge every 8th
+// chunk (loads four chunks ahead of the merges), then a fixed tree joins the lanes; the exact
+// sum is divided by S in fp64 and rounded once.
+constexpr int kMeanCh = 32;                  // channels per workgroup
+constexpr int kMeanLanes = kThreads / kMeanCh;
+
 template <int D>
 __global__ __launch_bounds__(kThreads) void kmean_final_kernel(const double* __restrict__ partial,
                                                                float* __restrict__ k_mean, int S,
                                                                int nch) {
-  constexpr int L = kThreads / D;  // lanes per channel
   __shared__ double sh[kThreads], sl[kThreads];
-  const int bh = blockIdx.x;
+  const int bh = blockIdx.x / (D / kMeanCh);
+  const int d = (blockIdx.x % (D / kMeanCh)) * kMeanCh + threadIdx.x % kMeanCh;
   const int tid = threadIdx.x;
-  const int d = tid % D, part = tid / D;
+  const int part = tid / kMeanCh;
+  const double* p = partial + 2 * ((size_t)bh * nch * D + d);
   DDSum s;
-  for (int c = part; c < nch; c += L) {
-    const double* p = partial + 2 * (((size_t)bh * nch + c) * D + d);
-    s.merge(p[0], p[1]);
+  int c = part;
+  for (; c + 3 * kMeanLanes < nch; c += 4 * kMeanLanes) {
+    double x[4][2];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      x[u][0] = p[2 * (size_t)(c + u * kMeanLanes) * D];
+      x[u][1] = p[2 * (size_t)(c + u * kMeanLanes) * D + 1];
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) s.merge(x[u][0], x[u][1]);
   }
+  for (; c < nch; c += kMeanLanes) s.merge(p[2 * (size_t)c * D], p[2 * (size_t)c * D + 1]);
   sh[tid] = s.hi;
   sl[tid] = s.lo;
   __syncthreads();
 #pragma unroll
-  for (int w = L / 2; w >= 1; w >>= 1) {
+  for (int w = kMeanLanes / 2; w >= 1; w >>= 1) {
     if (part < w) {
       DDSum t{sh[tid], sl[tid]};
-      t.merge(sh[tid + w * D], sl[tid + w * D]);
+      t.merge(sh[tid + w * kMeanCh], sl[tid + w * kMeanCh]);
       sh[tid] = t.hi;
       sl[tid] = t.lo;
     }
     __syncthreads();
   }
-  // sh[d] is the exact channel sum rounded once to fp64
-  if (part == 0) k_mean[(size_t)bh * D + d] = (float)(sh[d] / (double)S);
+  // sh[tid] (part 0) is the exact channel sum rounded once to fp64
+  if (part == 0) k_mean[(size_t)bh * D + d] = (float)(sh[tid] / (double)S);
 }
 
 // ---- per-block quantization --------------------------------------------------------------
@@ -385,8 +398,8 @@ hipError_t launch_prepass_d(const uint16_t* q, Strides qs, const uint16_t* k, St
   hipLaunchKernelGGL((kmean_partial_quant_q_kernel<D, FP8>),
                      dim3((unsigned)((long long)BH * (nch + nqb))), dim3(kThreads), 0, stream, q, qs,
                      k, ks, H, partial, q_codes, q_scale, S, BH, nch, rows_per, nqb);
-  hipLaunchKernelGGL(kmean_final_kernel<D>, dim3((unsigned)BH), dim3(kThreads), 0, stream, partial,
-                     k_mean, S, nch);
+  hipLaunchKernelGGL(kmean_final_kernel<D>, dim3((unsigned)(BH * (D / kMeanCh))), dim3(kThreads), 0,
+                     stream, partial, k_mean, S, nch);
   hipLaunchKernelGGL((quant_k_kernel<D, FP8>), dim3((unsigned)((long long)BH * nkb)), dim3(kThreads),
                      0, stream, k, ks, H, k_mean, k_codes, k_scale, S, nkb);
   return hipGetLastError();
