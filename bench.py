@@ -105,17 +105,36 @@ def cpu_baseline(budget_s=15.0):
         total_rows += rows
         rows = min(rows * 2, 4096)
     tflops = 4.0 * total_rows * S * D / t_attn / 1e12
+    # the int8-QK oracle on the same head: K mean, codes and scales for the whole head, then
+    # attention on the codes for a block of query rows
+    t0 = time.perf_counter()
+    qq = oracle.quantize_qk(qf, kf)
+    t_quant = time.perf_counter() - t0
+    rows8 = 1024
+    t0 = time.perf_counter()
+    oracle.attention_int8(qq["q_codes"], qq["q_scale"], qq["k_codes"], qq["k_scale"], vf,
+                          rows=np.arange(rows8))
+    t_int8 = time.perf_counter() - t0
     a, b = datagen.residual_pair(4096, 3072)
     af, bf = datagen.bf16_to_f64(a), datagen.bf16_to_f64(b)
     t0 = time.perf_counter()
     oracle.rel_l1(af, bf)
     t_rl1 = time.perf_counter() - t0
+    cpu_model = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            cpu_model = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")), "")
+    except OSError:
+        pass
     return {
         "value": tflops, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
         "sample": (f"fp64 exact attention (numpy/BLAS) for {total_rows} query rows of one head "
                    f"at S=118800, D=128 against all keys, {t_attn:.1f} s; rel-L1 over "
                    f"[4096, 3072] bf16 residuals {4 * 4096 * 3072 / t_rl1 / 1e9:.2f} GB/s"),
         "full_step_seconds_extrapolated": 2 * attn_flops(1, 24, S, D) / (tflops * 1e12),
+        "int8_oracle": {"quantize_head_s": t_quant, "rows": rows8,
+                        "tops": 4.0 * rows8 * S * D / t_int8 / 1e12},
+        "cpu_model": cpu_model, "affinity_cpus": len(os.sched_getaffinity(0)),
     }
 
 
