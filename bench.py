@@ -157,7 +157,16 @@ def time_image_shape(torch, dta, stream, ev, iters=50):
         e1.record(stream)
         torch.cuda.synchronize()
         ms = e0.elapsed_time(e1) / iters
-        out[name] = {"ms": ms, "tflops": attn_flops(B, H, S, D) / (ms * 1e-3) / 1e12}
+        # then each call between its own events, for the median
+        marks = [ev() for _ in range(iters + 1)]
+        marks[0].record(stream)
+        for i in range(iters):
+            fn()
+            marks[i + 1].record(stream)
+        torch.cuda.synchronize()
+        per_call = sorted(marks[i].elapsed_time(marks[i + 1]) for i in range(iters))
+        out[name] = {"ms": ms, "ms_median": per_call[iters // 2],
+                     "tflops": attn_flops(B, H, S, D) / (ms * 1e-3) / 1e12}
     out["bf16"]["frac_bf16_peak"] = out["bf16"]["tflops"] / PEAK_BF16_TFLOPS
     out["int8qk"]["frac_int8_peak"] = out["int8qk"]["tflops"] / PEAK_INT8_TOPS
     out["int8qk"]["frac_mixed_ceiling"] = out["int8qk"]["tflops"] / PEAK_INT8_BF16PV_TOPS
@@ -338,6 +347,7 @@ def main():
     ms_bf16 = sum(m[0].elapsed_time(m[1]) for m in marks) / args.steps
     ms_int8 = sum(m[1].elapsed_time(m[2]) for m in marks) / args.steps
     ms_rl1 = sum(m[2].elapsed_time(m[3]) for m in marks) / args.steps
+    median = lambda i: sorted(m[i].elapsed_time(m[i + 1]) for m in marks)[args.steps // 2]  # noqa: E731
     F = attn_flops(B, H, S, D)
     value = 2 * F / (ms_step * 1e-3) / 1e12
     bf16_tflops = F / (ms_bf16 * 1e-3) / 1e12
@@ -379,12 +389,15 @@ def main():
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": bf16_tflops / PEAK_BF16_TFLOPS, "traffic": traffic},
         "extra": {
-            "bf16": {"ms": ms_bf16, "tflops": bf16_tflops, "frac_bf16_peak": bf16_tflops / PEAK_BF16_TFLOPS},
-            "int8qk": {"ms": ms_int8, "tops": int8_tops, "frac_int8_peak": int8_tops / PEAK_INT8_TOPS,
+            "bf16": {"ms": ms_bf16, "ms_median": median(0), "tflops": bf16_tflops,
+                     "frac_bf16_peak": bf16_tflops / PEAK_BF16_TFLOPS},
+            "int8qk": {"ms": ms_int8, "ms_median": median(1), "tops": int8_tops,
+                       "frac_int8_peak": int8_tops / PEAK_INT8_TOPS,
                        "frac_mixed_ceiling": int8_tops / PEAK_INT8_BF16PV_TOPS,
                        "note": "whole call: K mean + quantization + attention; the mixed ceiling "
                                "is int8 QK plus bf16 PV at both peaks, 3333 TOPS"},
-            "rel_l1": {"ms": ms_rl1, "gbs": rl1_gbs, "frac_hbm_peak": rl1_gbs / PEAK_HBM_GBS},
+            "rel_l1": {"ms": ms_rl1, "ms_median": median(2), "gbs": rl1_gbs,
+                       "frac_hbm_peak": rl1_gbs / PEAK_HBM_GBS},
             "image_S4608": img,
             "fbcache_118800x3072": fbc,
             "quant_probe": probe,
