@@ -106,6 +106,30 @@ def test_fp8_ragged_lengths(S, D):
               f"S={S} D={D}")
 
 
+@pytest.mark.parametrize("scale", [0.02, 1.0])
+def test_fp8_nondefault_scale(scale):
+    """The softmax scale is an argument: fp8 QK, and QK and PV, against the oracle at it."""
+    B, H, S, D = 1, 2, 700, 128
+    announce(f"attn_fwd_fp8qk / attn_fwd_fp8 scale {scale} B{B} H{H} S{S} D{D}")
+    q = datagen.normal_bf16((B, H, S, D), 870, 0)
+    k = datagen.f64_to_bf16_bits(f64(datagen.normal_bf16((B, H, S, D), 870, 1)) + 0.5)
+    v = datagen.normal_bf16((B, H, S, D), 870, 2)
+    exact = oracle.attention(f64(q), f64(k), f64(v), scale=scale)
+    out, views = run_fp8(q, k, v, scale=scale)
+    ref = oracle.quantize_qk_fp8(f64(q), f64(k))
+    check_quant_exact(views, ref, f"scale {scale}")
+    oq = oracle.attention_fp8(ref["q_codes"], ref["q_scale"], ref["k_codes"], ref["k_scale"], f64(v),
+                              scale=scale)
+    check_out(out.cpu().numpy(), oq, exact, f"fp8 QK scale {scale}")
+    out, views = run_fp8_all(q, k, v, scale=scale)
+    ref, vc, vs = check_all_exact(views, q, k, v, f"fp8 all scale {scale}")
+    vq = oracle.e4m3_value(vc) * vs[:, :, None, :]
+    oqa = oracle.attention_fp8_full(ref["q_codes"], ref["q_scale"], ref["k_codes"], ref["k_scale"],
+                                    vc, vs, scale=scale)
+    check_out_model(out.cpu().numpy(), oqa, exact, fp8_pv_error_model(ref, vq, scale=scale),
+                    f"fp8 all scale {scale}")
+
+
 def test_fp8_outlier_blocks_and_tiny_values():
     """Blocks holding one large outlier next to tiny values: the e4m3 grid keeps the small
     values (subnormal codes included), and the codes stay bit-exact."""

@@ -226,6 +226,26 @@ def test_int8_ragged_lengths(S, D):
     check_int8_out(out.cpu().numpy(), oq, oracle.attention(f64(q), f64(k), f64(v)), f"S={S} D={D}")
 
 
+@pytest.mark.parametrize("scale", [0.02, 0.3, 1.0])
+@pytest.mark.parametrize("D", [64, 128])
+def test_nondefault_scale_both_paths(scale, D):
+    """The softmax scale is an argument: small (nearly uniform weights), large (peaked, the
+    running maximum moves often) and 1.0, on both paths against the oracle at that scale."""
+    S = 700
+    announce(f"attn_fwd_bf16 / attn_fwd_int8qk scale {scale} B1 H2 S{S} D{D}")
+    q = datagen.normal_bf16((1, 2, S, D), 600 + D, 0)
+    k = datagen.f64_to_bf16_bits(f64(datagen.normal_bf16((1, 2, S, D), 600 + D, 1)) + 0.5)
+    v = datagen.normal_bf16((1, 2, S, D), 600 + D, 2)
+    exact = oracle.attention(f64(q), f64(k), f64(v), scale=scale)
+    check_bf16(run_bf16(q, k, v, scale=scale).cpu().numpy(), exact, f"bf16 scale {scale} D={D}")
+    out, views = run_int8(q, k, v, scale=scale)
+    ref = oracle.quantize_qk(f64(q), f64(k))
+    check_quant_exact(views, ref, f"scale {scale} D={D}")
+    oq = oracle.attention_int8(ref["q_codes"], ref["q_scale"], ref["k_codes"], ref["k_scale"], f64(v),
+                               scale=scale)
+    check_int8_out(out.cpu().numpy(), oq, exact, f"int8 scale {scale} D={D}")
+
+
 def test_int8_zero_scale_guard_cases():
     S, D = 4608, 128
     q = datagen.normal_bf16((1, 2, S, D), 500, 0)
