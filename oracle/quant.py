@@ -293,9 +293,10 @@ def log_sum_exp_fp8(q_codes, q_scale, k_codes, k_scale, scale: float | None = No
 #   V: one scale per (b, h, channel) over all S tokens, scale_v = amax / 448 (1.0 if amax == 0),
 #      code = e4m3(clamp(fl32(v / scale_v), -448, 448)), rounded once (as the Q / K codes).
 #   o_i = sum_j p_ij * vq_jd * scale_v[d] / sum_j p_ij  with p the exact softmax weights of the
-#      fp8 scores.  (The GPU rounds each weight to e4m3 at its running offset before the product;
-#      that rounding is not part of this definition: it perturbs every weight by at most 2^-4
-#      relative, and the parity tolerance covers it.)
+#      fp8 scores.  (The GPU rounds each weight to e4m3 at its running offset before the product
+#      and normalises by the sum of those rounded weights; that rounding is not part of this
+#      definition: it perturbs every weight by at most 2^-4 relative, and the parity tolerance
+#      covers it.)
 
 def quantize_v_fp8(v):
     """Per-(b, h, channel) e4m3 codes of V: (codes uint8 [B, H, S, D], scales float32 [B, H, D])."""

@@ -175,8 +175,27 @@ def test_full_fp8_attention_reduces_to_exact_attention():
     got = oracle.attention_fp8_full(qq["q_codes"], qq["q_scale"], qq["k_codes"], qq["k_scale"],
                                     vc, vs, sc)
     np.testing.assert_allclose(got, oracle.attention(q, k, v, sc), rtol=1e-12, atol=1e-9)
-    # and a V scale that is not 1 is applied per channel
-    vc2, vs2 = oracle.quantize_v_fp8(v * 0.25)
+    # and V scales that are not 1 are applied per channel: a power of two per channel keeps the
+    # codes and scales exact, and each output channel scales by its own factor
+    f = 2.0 ** (np.arange(D) % 7 - 3.0)
+    vc2, vs2 = oracle.quantize_v_fp8(v * f)
+    assert np.array_equal(vs2[0, 0], f.astype(np.float32)) and np.array_equal(vc2, vc)
     got2 = oracle.attention_fp8_full(qq["q_codes"], qq["q_scale"], qq["k_codes"], qq["k_scale"],
                                      vc2, vs2, sc)
-    np.testing.assert_allclose(got2, 0.25 * got, rtol=1e-12, atol=1e-9)
+    np.testing.assert_allclose(got2, got * f, rtol=1e-12, atol=1e-9)
+
+
+def test_fp8_k_smoothing_invariance():
+    # a per-channel constant added to K moves the K mean by that constant and leaves the
+    # smoothed K, hence its codes and scales, unchanged (S a power of two and dyadic values, so
+    # the mean and every difference are exact in fp32)
+    rng = np.random.default_rng(46)
+    S, D = 256, 16
+    k = np.round(rng.standard_normal((1, 2, S, D)) * 64) / 64
+    q = np.round(rng.standard_normal((1, 2, S, D)) * 64) / 64
+    c = np.round(rng.standard_normal((1, 2, 1, D)) * 8) * 4          # multiples of 4, up to ~100
+    a = oracle.quantize_qk_fp8(q, k)
+    b = oracle.quantize_qk_fp8(q, k + c)
+    np.testing.assert_array_equal(b["k_mean"], (a["k_mean"] + c[:, :, 0].astype(np.float32)))
+    assert np.array_equal(b["k_codes"], a["k_codes"]) and np.array_equal(b["k_scale"], a["k_scale"])
+    assert np.array_equal(b["q_codes"], a["q_codes"])
