@@ -131,7 +131,8 @@ DITATTN_API int attn_fwd_fp8qk(const void* q, const void* k, const void* v, floa
  *               [8] scratch (partial channel maxima)
  * o[b,h,i,d] = sum_j p_ij vq[b,h,j,d] v_scale[b,h,d] / sum_j p_ij with p the softmax weights of
  * the fp8 scores.  Each weight enters the product rounded to e4m3 at the kernel's running
- * offset (at most 2^-4 relative; the row sum uses the fp32 weights). */
+ * offset (at most 2^-4 relative), and the row sum adds those same rounded weights, so the
+ * weights of a row sum to one (a V constant over the keys comes back unchanged). */
 DITATTN_API size_t attn_fp8_workspace_bytes(int B, int H, int S, int D);
 DITATTN_API size_t attn_fp8_workspace_offsets(int B, int H, int S, int D, size_t offsets[9]);
 DITATTN_API int attn_fwd_fp8(const void* q, const void* k, const void* v, float* o,
