@@ -1,5 +1,5 @@
 // Non-causal multi-head attention forward for gfx950 (MI355X): bf16, int8-QK and fp8-QK
-// variants.
+// variants, and fp8 for both products.
 //
 // O = softmax(Q K^T * scale) V, computed blockwise on chip so the S x S score matrix never
 // reaches HBM (the IO-aware tiling of the "Flash Attention 2 for Z-Image S3-DiT" page, method
@@ -18,6 +18,9 @@
 //     O^T += V^T P^T (bf16 MFMA), no LDS round trip for P.  Inside each 16-key step its key
 //     order is a fixed permutation, and the V^T A operand is read from LDS in that order
 //     with ds_read_b64_tr_b16 (gfx950's transposing LDS read), so V stays row-major in LDS.
+//     With fp8 V the weights are packed to e4m3 bytes and PV is one
+//     v_mfma_f32_32x32x64_f8f6f4 per 32 channels, its V^T operand read with ds_read_b64_tr_b8;
+//     each lane's sum of its rounded weights is one 16x16x128 fp8 product.
 //   * K and V tiles of 64 keys go straight from global memory into LDS with
 //     global_load_lds_dwordx4 (no VGPR staging).  Each wave writes 1 KB contiguously per
 //     instruction, so the XOR swizzle of 16-byte chunks is applied to the *global* address a
