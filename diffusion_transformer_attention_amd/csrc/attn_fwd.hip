@@ -46,6 +46,7 @@
 
 #include "device_common.h"
 #include "kernels.h"
+#include "scale_index.h"
 
 namespace ditattn {
 
@@ -93,6 +94,7 @@ struct Tile {
   static constexpr int NQF = INT8 ? D / 32 : D / 16;   // 16-byte Q fragments per lane
   static constexpr int NDB = D / 32;                   // 32-channel output blocks
   static_assert(KCH <= 16, "tile shape");
+  static_assert(kScaleQBlock == kQBlock && kScaleKBlock == kBK, "scale blocks");
 };
 
 // Swizzled chunk of K row `key`: 16 consecutive rows read at one logical chunk land in 16
@@ -226,7 +228,7 @@ void attn_fwd_kernel(const uint8_t* __restrict__ qp, const uint8_t* __restrict__
   float cq = c;
   if constexpr (INT8) {
     const int nqb = (Sq + kQBlock - 1) / kQBlock;  // (the int8 path never samples: Sq = Sk)
-    cq = q_scale[(size_t)bh * nqb + (qt * kBQ + wave * 32) / kQBlock] * c;
+    cq = q_scale[(size_t)bh * nqb + q_scale_block(qt, wave, kBQ, nqb)] * c;
   }
 
   // ---- direct global -> LDS tile loads ------------------------------------------------
@@ -428,7 +430,7 @@ void attn_fwd_kernel(const uint8_t* __restrict__ qp, const uint8_t* __restrict__
   auto weights = [&](int jt, const float (&s)[32], bf16x8 (&pb)[4], float& lt, float& cf)
                      __attribute__((always_inline)) {
     cf = cq;
-    if constexpr (INT8) cf = cq * k_scale[(size_t)bh * nkt + min(jt, nkt - 1)];
+    if constexpr (INT8) cf = cq * k_scale[(size_t)bh * nkt + k_scale_block(jt, nkt)];
     // exponent offset: m_run, plus the bias carried by the int8 scores (cf * kBiasF, rounded
     // once; its error is far below the int8 quantization error of the scores themselves)
     const float mb = I8 ? fmaf(cf, kBiasF, m_run) : m_run;

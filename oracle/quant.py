@@ -93,14 +93,6 @@ def quantize_blocks(x, block: int):
     return codes, scales
 
 
-def dequantize_blocks(codes, scales, block: int) -> np.ndarray:
-    """codes * scale of their block, fp64 [B, H, S, D]."""
-    codes = np.asarray(codes)
-    S = codes.shape[2]
-    per_tok = np.repeat(np.asarray(scales, dtype=np.float64), block, axis=2)[:, :, :S]
-    return codes.astype(np.float64) * per_tok[..., None]
-
-
 def quantize_qk(q, k, kmean=None):
     """Rules 1-5 applied to Q and K (fp64 arrays holding bf16 values, [B, H, S, D]).
 
