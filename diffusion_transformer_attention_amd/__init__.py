@@ -13,6 +13,7 @@ Entry points (same names as the C ABI in include/ditattn.h):
   attn_fwd_fp8qk(q, k, v, out=None, scale=None, workspace=None) -> out
   attn_fwd_fp8(q, k, v, out=None, scale=None, workspace=None) -> out   (fp8 QK and PV, D = 128)
   resid_rel_l1(a, b, out=None, workspace=None) -> out (fp32 device scalar, shape [1])
+  resid_rel_l1_noalloc(a, b, out) -> out (same result; no workspace, no allocation)
   attn_quant_probe(q, k, v, o_q, n_rows=256, scale=None) -> err (fp32 [1 + B*H])
   fbcache_decide(resid, prev_resid, state, config, workspace=None) -> state
   resid_add(a, b, out=None) -> out;  resid_sub(a, b, out=None) -> out
@@ -35,7 +36,7 @@ import os
 import torch  # loaded first: the library then binds to the HIP runtime torch already holds
 
 __all__ = ["attn_fwd_bf16", "attn_fwd_int8qk", "attn_fwd_fp8qk", "attn_fwd_fp8", "fp8_workspace",
-           "fp8_views", "resid_rel_l1", "int8qk_workspace",
+           "fp8_views", "resid_rel_l1", "resid_rel_l1_noalloc", "int8qk_workspace",
            "int8qk_views", "int8qk_workspace_bytes", "rel_l1_workspace_bytes", "fbcache_decide",
            "resid_add", "resid_sub", "FBCacheConfig", "fbcache_state", "fbcache_state_values",
            "attn_quant_probe", "quant_probe_workspace_bytes", "quant_probe_views",
@@ -105,6 +106,8 @@ def lib() -> ctypes.CDLL:
     L.resid_rel_l1_workspace_bytes.restype = sz
     L.resid_rel_l1.argtypes = [vp, vp, i64, vp, vp, sz, vp]
     L.resid_rel_l1.restype = i
+    L.resid_rel_l1_noalloc.argtypes = [vp, vp, i64, vp, vp]
+    L.resid_rel_l1_noalloc.restype = i
     L.attn_quant_probe_splits.argtypes = [i, i, i, i, i]
     L.attn_quant_probe_splits.restype = i
     L.attn_quant_probe_workspace_bytes.argtypes = [i, i, i, i, i]
@@ -322,6 +325,21 @@ def resid_rel_l1(a, b, out=None, workspace=None):
         workspace = torch.empty(max(rel_l1_workspace_bytes(n), 1), dtype=torch.uint8, device=a.device)
     _check(lib().resid_rel_l1(_ptr(a), _ptr(b), n, _ptr(out), _ptr(workspace), workspace.numel(),
                               _stream(a)))
+    return out
+
+
+def resid_rel_l1_noalloc(a, b, out):
+    """resid_rel_l1 through the allocation-free entry point: the caller passes the fp32 device
+    tensor [1] for the result; the library keeps the partial sums in its own static device
+    array (calls that overlap on one GPU race)."""
+    for name, t in (("a", a), ("b", b)):
+        if not t.is_cuda or t.dtype != torch.bfloat16 or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous bf16 CUDA tensor")
+    if a.shape != b.shape:
+        raise ValueError("a and b must have the same shape")
+    if not out.is_cuda or out.dtype != torch.float32 or out.numel() < 1:
+        raise ValueError("out must be an fp32 CUDA tensor of at least one element")
+    _check(lib().resid_rel_l1_noalloc(_ptr(a), _ptr(b), a.numel(), _ptr(out), _stream(a)))
     return out
 
 

@@ -304,6 +304,13 @@ int resid_rel_l1(const void* a, const void* b, int64_t n, float* out, void* work
                                           static_cast<hipStream_t>(stream)));
 }
 
+int resid_rel_l1_noalloc(const void* a, const void* b, int64_t n, float* out, void* stream) {
+  if (!a || !b || !out || n < 1) return DITATTN_EINVAL;
+  if (!aligned(a, 16) || !aligned(b, 16) || !aligned(out, 4)) return DITATTN_EINVAL;
+  if ((size_t)ditattn::rel_l1_blocks(n) > ditattn::rel_l1_static_pairs()) return DITATTN_EWORKSPACE;
+  return status_of(ditattn::launch_rel_l1_static(a, b, n, out, static_cast<hipStream_t>(stream)));
+}
+
 int attn_quant_probe_splits(int B, int H, int S, int D, int n_rows) {
   if (check_attn_shape(B, H, S, D) != DITATTN_OK || n_rows < 1 || n_rows > S) return 0;
   return ditattn::probe_chunks(B, H, S, n_rows).ns;

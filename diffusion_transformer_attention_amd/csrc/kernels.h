@@ -73,6 +73,14 @@ int rel_l1_blocks(int64_t n);
 hipError_t launch_rel_l1(const void* a, const void* b, int64_t n, float* out, double* partial,
                          hipStream_t stream);
 
+// Partial pairs the static scratch array of launch_rel_l1_static holds.
+size_t rel_l1_static_pairs();
+
+// launch_rel_l1 with the partial pairs in the library's static per-device array (no
+// allocation, no workspace); calls that overlap on one GPU race.
+hipError_t launch_rel_l1_static(const void* a, const void* b, int64_t n, float* out,
+                                hipStream_t stream);
+
 // The relative-L1 pass of resid against prev_resid (skipped when prev_resid is null) followed by
 // one First Block Cache decision on *state (device memory).  partial: rel_l1_blocks(n) pairs.
 hipError_t launch_fbcache_decide(const void* resid, const void* prev_resid, int64_t n,

@@ -13,6 +13,8 @@
 // of the step: reuse only past the warmup steps, with a difference below the threshold, and
 // within the caps on cached and consecutively cached steps (DBCache parameters of the
 // "Cache-DiT acceleration" page).  The decision and the counters stay in device memory.
+#include <mutex>
+
 #include "device_common.h"
 #include "kernels.h"
 
@@ -163,6 +165,63 @@ __global__ __launch_bounds__(kThreads) void fbcache_final_kernel(const double* _
 }
 
 }  // namespace
+
+// ---- the allocation-free variant: partial sums in a static device array ---------------------
+// For callers that cannot allocate device memory, the partial pairs go to this file-scope
+// array: kMaxBlocks pairs (64 KiB), the most any n needs, one copy per GPU the library runs on,
+// held until the process ends.  Its name is a host-side stand-in, not a device address: the
+// address of each device's copy is looked up once (with that device current) and only that
+// looked-up pointer reaches the kernels.  Every call on a GPU shares the array, so calls that
+// overlap on one GPU race; nothing in it needs clearing, because the finishing kernel reads
+// only the pairs the same call's partial kernel has just written.
+static __device__ __align__(256) double scratch[2 * kMaxBlocks];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+double* g_scratch[kMaxDevices] = {};
+
+// This device's copy of `scratch`, the device being the one `stream` belongs to (the current
+// device for the null stream).
+hipError_t scratch_for(hipStream_t stream, double** out) {
+  int cur = 0;
+  hipError_t e = hipGetDevice(&cur);
+  if (e != hipSuccess) return e;
+  int dev = cur;
+  if (stream != nullptr) {
+    e = hipStreamGetDevice(stream, &dev);
+    if (e != hipSuccess) return e;
+  }
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch[dev] == nullptr) {
+    if (dev != cur && (e = hipSetDevice(dev)) != hipSuccess) return e;
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (dev != cur) {
+      const hipError_t e2 = hipSetDevice(cur);
+      if (e == hipSuccess) e = e2;
+    }
+    if (e != hipSuccess) return e;
+    g_scratch[dev] = static_cast<double*>(p);
+  }
+  *out = g_scratch[dev];
+  return hipSuccess;
+}
+
+}  // namespace
+
+size_t rel_l1_static_pairs() { return kMaxBlocks; }
+
+hipError_t launch_rel_l1_static(const void* a, const void* b, int64_t n, float* out,
+                                hipStream_t stream) {
+  if ((size_t)rel_l1_blocks(n) > rel_l1_static_pairs()) return hipErrorInvalidValue;
+  double* partial = nullptr;
+  const hipError_t e = scratch_for(stream, &partial);
+  if (e != hipSuccess) return e;
+  return launch_rel_l1(a, b, n, out, partial, stream);
+}
 
 int rel_l1_blocks(int64_t n) {
   const int64_t n8 = n >> 3;

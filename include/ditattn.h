@@ -202,6 +202,19 @@ DITATTN_API size_t resid_rel_l1_workspace_bytes(int64_t n);
 DITATTN_API int resid_rel_l1(const void* a, const void* b, int64_t n, float* out,
                  void* workspace, size_t workspace_bytes, void* stream);
 
+/* resid_rel_l1 for callers that cannot allocate device memory: code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc.  Same arguments without the workspace,
+ * same kernels, same result bits.  The partial sums go to a 64 KiB array in the library's own
+ * device memory instead: one copy per GPU, held from the library's load until the process ends.
+ * Every n fits (the pass uses at most 4096 partial pairs); a need beyond the array would be
+ * rejected with DITATTN_EWORKSPACE.  The call makes no allocation; its first call on a GPU
+ * looks up that GPU's copy of the array (hipGetSymbolAddress; DITATTN_EHIP if that fails).
+ * All calls on one GPU share the array: calls that overlap on a GPU (on different streams, or
+ * from threads without stream ordering) race and give wrong results.  `stream` may belong to
+ * any device; the array of that stream's device is used. */
+DITATTN_API int resid_rel_l1_noalloc(const void* a, const void* b, int64_t n, float* out,
+                                     void* stream);
+
 /* ---- quantization-error probe -----------------------------------------------------------
  *
  * Which attention layers may run quantized: the "TMAP image-to-video inference acceleration"

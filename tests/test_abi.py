@@ -33,9 +33,9 @@ def test_header_declares_the_three_calls():
     for n in ("attn_fwd_bf16", "attn_fwd_int8qk", "resid_rel_l1", "attn_fwd_bf16_ex",
               "attn_fwd_int8qk_ex", "fbcache_decide", "resid_add", "resid_sub",
               "attn_quant_probe", "attn_fwd_fp8qk", "attn_fwd_fp8qk_ex", "attn_fwd_fp8",
-              "attn_fwd_fp8_ex"):
+              "attn_fwd_fp8_ex", "resid_rel_l1_noalloc"):
         assert n in names
-    assert len(names) == 21
+    assert len(names) == 22
 
 
 def test_library_exports_every_declared_symbol(L):
@@ -195,6 +195,18 @@ def test_rel_l1_argument_errors(L):
     assert L.resid_rel_l1(FAKE + 2, FAKE + 0x100, 100, FAKE + 0x1000, FAKE + 0x2000, need, None) == EINVAL
     assert L.resid_rel_l1(FAKE, FAKE + 0x100, 100, FAKE + 0x1000, None, need, None) == EWS
     assert L.resid_rel_l1(FAKE, FAKE + 0x100, 100, FAKE + 0x1000, FAKE + 0x2000, need - 1, None) == EWS
+
+
+def test_rel_l1_noalloc_argument_errors(L):
+    # rejected before any HIP call (the device array is only looked up for a valid call)
+    assert L.resid_rel_l1_noalloc(None, FAKE, 100, FAKE + 0x1000, None) == EINVAL
+    assert L.resid_rel_l1_noalloc(FAKE, None, 100, FAKE + 0x1000, None) == EINVAL
+    assert L.resid_rel_l1_noalloc(FAKE, FAKE + 0x100, 100, None, None) == EINVAL
+    assert L.resid_rel_l1_noalloc(FAKE, FAKE + 0x100, 0, FAKE + 0x1000, None) == EINVAL
+    assert L.resid_rel_l1_noalloc(FAKE, FAKE + 0x100, -5, FAKE + 0x1000, None) == EINVAL
+    assert L.resid_rel_l1_noalloc(FAKE + 2, FAKE + 0x100, 100, FAKE + 0x1000, None) == EINVAL
+    assert L.resid_rel_l1_noalloc(FAKE, FAKE + 0x108, 100, FAKE + 0x1000, None) == EINVAL
+    assert L.resid_rel_l1_noalloc(FAKE, FAKE + 0x100, 100, FAKE + 0x1002, None) == EINVAL
 
 
 def test_quant_probe_workspace_and_errors(L):
