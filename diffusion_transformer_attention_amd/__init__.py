@@ -75,7 +75,12 @@ def lib() -> ctypes.CDLL:
     if not os.path.exists(LIB_PATH):
         raise RuntimeError(f"{LIB_PATH} is not built; run "
                            "`python -m diffusion_transformer_attention_amd.build`")
-    L = ctypes.CDLL(LIB_PATH)
+    _lib = declare(ctypes.CDLL(LIB_PATH))
+    return _lib
+
+
+def declare(L: ctypes.CDLL) -> ctypes.CDLL:
+    """Declare the C ABI's signatures (include/ditattn.h) on a loaded copy of the library."""
     vp, i, f, sz, i64 = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t, ctypes.c_int64
     L.attn_fwd_bf16.argtypes = [vp, vp, vp, vp, i, i, i, i, f, vp]
     L.attn_fwd_bf16.restype = i
@@ -122,7 +127,6 @@ def lib() -> ctypes.CDLL:
     L.resid_sub.restype = i
     L.ditattn_status_string.argtypes = [i]
     L.ditattn_status_string.restype = ctypes.c_char_p
-    _lib = L
     return L
 
 

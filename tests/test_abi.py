@@ -17,6 +17,11 @@ FAKE = 0x100000  # a 256-byte aligned address the library never dereferences on 
 @pytest.fixture(scope="module")
 def L():
     import diffusion_transformer_attention_amd as dta
+    # DITATTN_ABI_LIB: run these checks on another build of the same sources, e.g. the
+    # host-instrumented one of tests/run_abi_asan.py
+    alt = os.environ.get("DITATTN_ABI_LIB")
+    if alt:
+        return dta.declare(ctypes.CDLL(alt))
     if not os.path.exists(dta.LIB_PATH):
         from diffusion_transformer_attention_amd.build import build
         build()
