@@ -4,9 +4,13 @@ One step = the whole path once over one batch of resident synthetic input:
   attn_fwd_bf16    B=1 H=24 S=118800 D=128 (a 720p 129-frame video latent)
   attn_fwd_int8qk  same tensors (K mean, int8 quantization and int8-QK attention)
   resid_rel_l1     two bf16 [118800, 3072] first-block residuals
-Throughput counts 4*B*H*S^2*D flops per attention call; `value` is the counted flops of both
-attention calls per step divided by the step time (the rel-L1 pass is inside the step).
-The image-DiT shape (S=4608) is timed after the main loop and reported in `extra`.
+Throughput counts 4*B*H*S^2*D flops per attention call.  `value` is the bf16 call's TFLOP/s
+(the mean of its per-step HIP-event times): one precision, one kernel.  The int8-QK call (TOPS,
+whole call including its prepass), the rel-L1 pass (GB/s), the image shape (S=4608) and the
+video shape (B=2, S=11440) on both paths are reported in `extra`, each with its fraction of
+the nominal peak, of the peak at the device's rated clock, and of the sustained matrix-core
+rate the library's calibration kernel measures in the same run (products alone on random
+operands: the chip's power limit).
 
 Prints ONE JSON line.  Options: --gpus N (only 1: this build runs on one GPU),
 --steps K, --warmup W, --no-cpu-baseline.
@@ -27,6 +31,13 @@ sys.path.insert(0, ROOT)
 PEAK_BF16_TFLOPS = 2500.0    # MI355X dense bf16 MFMA
 PEAK_INT8_TOPS = 5000.0      # MI355X dense int8 MFMA
 PEAK_HBM_GBS = 8000.0        # MI355X HBM3E
+# Per CU and clock: 4096 bf16 flops, 8192 int8 ops (32x32x16 bf16 / 32x32x32 int8 products in
+# 32 cycles on each of 4 SIMDs); with the rated clock these give the clock-derived peaks.
+FLOP_PER_CU_CLK = {"bf16": 4096.0, "int8": 8192.0}
+# The sustained matrix-core rates (what the chip delivers on products alone, random operands,
+# measured in every run with the library's calibration kernel, measure_mfma_sustained) are
+# filled in here before any fraction of them is computed.
+SUSTAINED = {}
 # The int8-QK call does half its counted flops (QK) on int8 MFMA and half (PV) on bf16 MFMA, so
 # even at both peaks it reaches only 1 / (0.5 / 5000 + 0.5 / 2500) = 3333 TOPS (66.7% of int8).
 PEAK_INT8_BF16PV_TOPS = 1.0 / (0.5 / PEAK_INT8_TOPS + 0.5 / PEAK_BF16_TFLOPS)
@@ -79,10 +90,62 @@ def load_traffic():
     return rec.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(budget_s=15.0):
-    """The fp64 oracle timed on the host cores on a bounded sample of the step's workload:
-    exact attention for a few query rows of one head at S=118800 (all keys), plus the
-    relative-L1 reduction over a slice of the residuals."""
+def device_env(torch):
+    """GPU, its compute units and rated clock, ROCm / torch versions and the library's source
+    revision (recorded by the build, since the benchmark machine has no git history)."""
+    import ctypes
+    props = torch.cuda.get_device_properties(0)
+    env = {"gpu": props.name, "arch": getattr(props, "gcnArchName", None),
+           "cus": props.multi_processor_count, "torch": torch.__version__,
+           "hip": getattr(torch.version, "hip", None)}
+    try:  # hipDeviceGetAttribute(&v, hipDeviceAttributeClockRate (5), device): peak clock, kHz
+        hip = ctypes.CDLL("libamdhip64.so")
+        v = ctypes.c_int(0)
+        if hip.hipDeviceGetAttribute(ctypes.byref(v), 5, torch.cuda.current_device()) == 0:
+            env["clock_khz_rated"] = v.value
+    except OSError:
+        pass
+    for path in ("/opt/rocm/.info/version",):
+        try:
+            with open(path) as f:
+                env["rocm"] = f.read().strip()
+        except OSError:
+            pass
+    try:
+        with open(os.path.join(ROOT, "diffusion_transformer_attention_amd", "build_info.json")) as f:
+            env.update(json.load(f))
+    except (OSError, ValueError):
+        env["git_sha"] = None
+    return env
+
+
+def _cpu_description():
+    """Model name, family / model / stepping numbers and logical CPUs from /proc/cpuinfo."""
+    fields = {}
+    try:
+        with open("/proc/cpuinfo") as f:
+            for ln in f:
+                if ":" in ln:
+                    key, val = (x.strip() for x in ln.split(":", 1))
+                    if key in ("model name", "cpu family", "model", "stepping", "cpu MHz") and key not in fields:
+                        fields[key] = val
+                if ln.strip() == "" and fields:
+                    break
+    except OSError:
+        pass
+    return {"model_name": fields.get("model name", ""), "family": fields.get("cpu family"),
+            "model": fields.get("model"), "stepping": fields.get("stepping"),
+            "mhz": fields.get("cpu MHz"), "logical_cpus": os.cpu_count(),
+            "affinity_cpus": len(os.sched_getaffinity(0))}
+
+
+def cpu_baseline():
+    """The fp64 oracle timed on the host cores, per workload, on bounded samples:
+    exact attention (C-1) and attention on the int8 codes (C-3) for whole heads of the tiny,
+    image and video workloads and for a block of query rows of one long-video head, the int8
+    quantization of that head, and the relative-L1 reduction (C-4) over a slice of the
+    residuals.  Each entry extrapolates to the full workload (rows are independent).  About
+    15-25 s of CPU work in all."""
     import numpy as np
     import datagen
     import oracle
@@ -91,56 +154,114 @@ def cpu_baseline(budget_s=15.0):
         threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
     except Exception:  # pragma: no cover - threadpoolctl missing
         threads = len(os.sched_getaffinity(0))
-    S, D = 118800, 128
-    wid = datagen.WORKLOADS["longvideo"][0]
-    off = datagen.k_offsets(wid, 1, D, 2.0)
-    q, k, v = datagen.qkv_head(wid, 0, 0, S, D, off[0])
-    qf, kf, vf = (datagen.bf16_to_f64(t)[None, None] for t in (q, k, v))
-    rows, total_rows, t_attn = 32, 0, 0.0
-    while t_attn < budget_s * 0.8:
-        sel = np.arange(total_rows, total_rows + rows) % S
+    f64 = datagen.bf16_to_f64
+    per = {}
+
+    def timed(fn):
         t0 = time.perf_counter()
-        oracle.attention_rows(qf, kf, vf, sel)
-        t_attn += time.perf_counter() - t0
-        total_rows += rows
-        rows = min(rows * 2, 4096)
-    tflops = 4.0 * total_rows * S * D / t_attn / 1e12
-    # the int8-QK oracle on the same head: K mean, codes and scales for the whole head, then
-    # attention on the codes for a block of query rows
-    t0 = time.perf_counter()
-    qq = oracle.quantize_qk(qf, kf)
-    t_quant = time.perf_counter() - t0
-    rows8 = 1024
-    t0 = time.perf_counter()
-    oracle.attention_int8(qq["q_codes"], qq["q_scale"], qq["k_codes"], qq["k_scale"], vf,
-                          rows=np.arange(rows8))
-    t_int8 = time.perf_counter() - t0
-    a, b = datagen.residual_pair(4096, 3072)
-    af, bf = datagen.bf16_to_f64(a), datagen.bf16_to_f64(b)
-    t0 = time.perf_counter()
-    oracle.rel_l1(af, bf)
-    t_rl1 = time.perf_counter() - t0
-    cpu_model = ""
-    try:
-        with open("/proc/cpuinfo") as f:
-            cpu_model = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")), "")
-    except OSError:
-        pass
+        fn()
+        return time.perf_counter() - t0
+
+    def head_inputs(name, h):
+        wid, B, H, S, D, var = datagen.WORKLOADS[name]
+        off = datagen.k_offsets(wid, H, D, var)
+        q, k, v = datagen.qkv_head(wid, 0, h, S, D, off[h] if var else None)
+        return tuple(f64(t)[None, None] for t in (q, k, v)), (B, H, S, D)
+
+    for name in ("tiny", "image", "video"):
+        (qf, kf, vf), (B, H, S, D) = head_inputs(name, 0)
+        t_exact = timed(lambda: oracle.attention(qf, kf, vf))
+        qq = {}
+        t_quant = timed(lambda: qq.update(oracle.quantize_qk(qf, kf)))
+        t_int8 = timed(lambda: oracle.attention_int8(qq["q_codes"], qq["q_scale"], qq["k_codes"],
+                                                     qq["k_scale"], vf))
+        heads = B * H
+        fl = attn_flops(1, 1, S, D)
+        per[name] = {"sample": f"one head of B{B} H{H} S{S} D{D}, every row",
+                     "exact_s": t_exact, "exact_tflops": fl / t_exact / 1e12,
+                     "int8_s": t_quant + t_int8, "int8_tops": fl / (t_quant + t_int8) / 1e12,
+                     "full_workload_s_extrapolated": heads * (t_exact + t_quant + t_int8)}
+    # long video: a block of query rows of one head against all 118800 keys, both oracles
+    (qf, kf, vf), (B, H, S, D) = head_inputs("longvideo", 0)
+    rows = np.arange(1024)
+    t_exact = timed(lambda: oracle.attention_rows(qf, kf, vf, rows))
+    qq = {}
+    t_quant = timed(lambda: qq.update(oracle.quantize_qk(qf, kf)))
+    t_int8 = timed(lambda: oracle.attention_int8(qq["q_codes"], qq["q_scale"], qq["k_codes"],
+                                                 qq["k_scale"], vf, rows=rows))
+    fl = 4.0 * rows.size * S * D
+    exact_tflops = fl / t_exact / 1e12
+    per["longvideo"] = {"sample": f"{rows.size} query rows of one head of B1 H24 S{S} D{D}, all keys; "
+                                  "int8: the head's K mean, codes and scales, then those rows",
+                        "exact_s": t_exact, "exact_tflops": exact_tflops,
+                        "int8_s": t_quant + t_int8, "int8_tops": fl / t_int8 / 1e12,
+                        "quantize_head_s": t_quant,
+                        "full_workload_s_extrapolated": 2 * attn_flops(1, 24, S, D) / (exact_tflops * 1e12)}
+    a, b = datagen.residual_pair(8192, 3072)
+    af, bf = f64(a), f64(b)
+    t_rl1 = timed(lambda: oracle.rel_l1(af, bf))
+    gbs = 4.0 * a.size / t_rl1 / 1e9
+    per["rel_l1"] = {"sample": "[8192, 3072] bf16 residual pair", "s": t_rl1, "gbs": gbs,
+                     "full_workload_s_extrapolated": 4.0 * 118800 * 3072 / (gbs * 1e9)}
     return {
-        "value": tflops, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
-        "sample": (f"fp64 exact attention (numpy/BLAS) for {total_rows} query rows of one head "
-                   f"at S=118800, D=128 against all keys, {t_attn:.1f} s; rel-L1 over "
-                   f"[4096, 3072] bf16 residuals {4 * 4096 * 3072 / t_rl1 / 1e9:.2f} GB/s"),
-        "full_step_seconds_extrapolated": 2 * attn_flops(1, 24, S, D) / (tflops * 1e12),
-        "int8_oracle": {"quantize_head_s": t_quant, "rows": rows8,
-                        "tops": 4.0 * rows8 * S * D / t_int8 / 1e12},
-        "cpu_model": cpu_model, "affinity_cpus": len(os.sched_getaffinity(0)),
+        "value": exact_tflops, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+        "sample": (f"fp64 exact attention (numpy/BLAS) for {rows.size} query rows of one head at "
+                   f"S=118800, D=128 against all keys, {t_exact:.1f} s; per-workload figures "
+                   "(tiny, image, video whole heads; int8 oracle; rel-L1) in per_config"),
+        "per_config": per, "cpu": _cpu_description(),
     }
 
 
-def time_image_shape(torch, dta, stream, ev, iters=50):
-    """bf16 and int8-QK attention at B1 H24 S4608 D128 (a 1024x1024 image DiT), ms per call."""
-    B, H, S, D = 1, 24, 4608, 128
+def measure_mfma_sustained(torch, dta, stream, ev):
+    """The library's calibration kernel (ditattn_mfma_probe: 1024 workgroups of 8 wavefronts
+    issuing independent 32x32 products and nothing else), timed on the stream: bf16 and int8
+    products on random operands (the power-limited rate real data gets; ~68 ms each) and bf16
+    on constant operands (the rated-clock rate; ~43 ms), each with the shader clock it ran at."""
+    out = {}
+    for dtype, rnd, iters in (("bf16", True, 50000), ("int8", True, 50000), ("bf16", False, 50000)):
+        clocks = dta.mfma_probe(dtype, rnd, iters=500)
+        torch.cuda.synchronize()
+        e0, e1 = ev(), ev()
+        e0.record(stream)
+        dta.mfma_probe(dtype, rnd, iters=iters, clocks=clocks)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1)
+        c = clocks.cpu()
+        rate = dta.mfma_probe_flops(dtype, iters) / (ms * 1e-3) / 1e12
+        nominal = PEAK_BF16_TFLOPS if dtype == "bf16" else PEAK_INT8_TOPS
+        out[f"{dtype}_{'random' if rnd else 'constant'}_operands"] = {
+            "ms": ms, "rate": rate, "frac_nominal_peak": rate / nominal,
+            "shader_clock_ghz": float(c[:, 0].sum()) / float(c[:, 1].sum()) * 0.1}
+    SUSTAINED["bf16"] = out["bf16_random_operands"]["rate"]
+    SUSTAINED["int8"] = out["int8_random_operands"]["rate"]
+    SUSTAINED["mixed"] = 1.0 / (0.5 / SUSTAINED["int8"] + 0.5 / SUSTAINED["bf16"])
+    out["int8qk_mixed_rate"] = SUSTAINED["mixed"]
+    out["note"] = ("products alone, every CU, two wavefronts per SIMD; rate in TFLOP/s (bf16) or "
+                   "TOPS (int8); the mixed rate is half the work at each random-operand rate, "
+                   "the most the int8-QK call (int8 QK, bf16 PV) could sustain")
+    return out
+
+
+def _fracs(rate, dtype, clock_khz, cus):
+    """Fractions of the nominal peak, of the peak at the rated clock and of the sustained
+    (power-limited) matrix-core rate measured in this run."""
+    nominal = PEAK_BF16_TFLOPS if dtype == "bf16" else PEAK_INT8_TOPS
+    out = {f"frac_{dtype}_peak": rate / nominal}
+    if dtype in SUSTAINED:
+        out[f"frac_{dtype}_sustained"] = rate / SUSTAINED[dtype]
+    if clock_khz and cus:
+        out[f"frac_{dtype}_clock_peak"] = rate / (cus * FLOP_PER_CU_CLK[dtype] * clock_khz * 1e3 / 1e12)
+    if dtype == "int8":
+        out["frac_mixed_ceiling"] = rate / PEAK_INT8_BF16PV_TOPS
+        if "mixed" in SUSTAINED:
+            out["frac_mixed_sustained"] = rate / SUSTAINED["mixed"]
+    return out
+
+
+def time_shape(torch, dta, stream, ev, B, H, S, D, iters, clock_khz, cus):
+    """bf16 and int8-QK attention at [B, H, S, D], ms per call: `iters` calls back to back for
+    the mean, then `iters` each between their own events for the median."""
     q, k, v = make_inputs(torch, B, H, S, D, seed=1)
     ws = dta.int8qk_workspace(B, H, S, D, "cuda")
     o = torch.empty((B, H, S, D), dtype=torch.float32, device="cuda")
@@ -157,7 +278,6 @@ def time_image_shape(torch, dta, stream, ev, iters=50):
         e1.record(stream)
         torch.cuda.synchronize()
         ms = e0.elapsed_time(e1) / iters
-        # then each call between its own events, for the median
         marks = [ev() for _ in range(iters + 1)]
         marks[0].record(stream)
         for i in range(iters):
@@ -165,11 +285,11 @@ def time_image_shape(torch, dta, stream, ev, iters=50):
             marks[i + 1].record(stream)
         torch.cuda.synchronize()
         per_call = sorted(marks[i].elapsed_time(marks[i + 1]) for i in range(iters))
-        out[name] = {"ms": ms, "ms_median": per_call[iters // 2],
-                     "tflops": attn_flops(B, H, S, D) / (ms * 1e-3) / 1e12}
-    out["bf16"]["frac_bf16_peak"] = out["bf16"]["tflops"] / PEAK_BF16_TFLOPS
-    out["int8qk"]["frac_int8_peak"] = out["int8qk"]["tflops"] / PEAK_INT8_TOPS
-    out["int8qk"]["frac_mixed_ceiling"] = out["int8qk"]["tflops"] / PEAK_INT8_BF16PV_TOPS
+        rate = attn_flops(B, H, S, D) / (ms * 1e-3) / 1e12
+        out[name] = {"ms": ms, "ms_median": per_call[iters // 2], "tflops": rate,
+                     **_fracs(rate, "bf16" if name == "bf16" else "int8", clock_khz, cus)}
+    del q, k, v, ws, o
+    torch.cuda.empty_cache()
     return out
 
 
@@ -349,14 +469,18 @@ def main():
     ms_rl1 = sum(m[2].elapsed_time(m[3]) for m in marks) / args.steps
     median = lambda i: sorted(m[i].elapsed_time(m[i + 1]) for m in marks)[args.steps // 2]  # noqa: E731
     F = attn_flops(B, H, S, D)
-    value = 2 * F / (ms_step * 1e-3) / 1e12
     bf16_tflops = F / (ms_bf16 * 1e-3) / 1e12
     int8_tops = F / (ms_int8 * 1e-3) / 1e12
+    value = bf16_tflops
     rl1_bytes = 4.0 * a.numel()
     rl1_gbs = rl1_bytes / (ms_rl1 * 1e-3) / 1e9
+    env = device_env(torch)
+    clk, cus = env.get("clock_khz_rated"), env.get("cus")
+    sustained = measure_mfma_sustained(torch, dta, stream, ev)
 
-    # image-DiT shape, timed separately (not part of `value`)
-    img = None if args.headline_only else time_image_shape(torch, dta, stream, ev)
+    # the image and video shapes, timed separately on both paths (not part of `value`)
+    img = None if args.headline_only else time_shape(torch, dta, stream, ev, 1, 24, 4608, 128, 50, clk, cus)
+    vid = None if args.headline_only else time_shape(torch, dta, stream, ev, 2, 24, 11440, 128, 10, clk, cus)
     fbc = None if args.headline_only else time_fbcache(torch, dta, stream, ev, a, b)
     probe = None if args.headline_only else time_probe(torch, dta, stream, ev, q, k, v, o_int8)
     fp8 = None if args.headline_only else time_fp8(torch, dta, stream, ev, q, k, v, o_int8, ws8)
@@ -389,16 +513,21 @@ def main():
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": bf16_tflops / PEAK_BF16_TFLOPS, "traffic": traffic},
         "extra": {
+            "value_is": "attn_fwd_bf16 TFLOP/s at B1 H24 S118800 D128 (mean of the per-step call "
+                        "times); the step also runs attn_fwd_int8qk and resid_rel_l1, below",
             "bf16": {"ms": ms_bf16, "ms_median": median(0), "tflops": bf16_tflops,
-                     "frac_bf16_peak": bf16_tflops / PEAK_BF16_TFLOPS},
+                     **_fracs(bf16_tflops, "bf16", clk, cus)},
             "int8qk": {"ms": ms_int8, "ms_median": median(1), "tops": int8_tops,
-                       "frac_int8_peak": int8_tops / PEAK_INT8_TOPS,
-                       "frac_mixed_ceiling": int8_tops / PEAK_INT8_BF16PV_TOPS,
+                       **_fracs(int8_tops, "int8", clk, cus),
                        "note": "whole call: K mean + quantization + attention; the mixed ceiling "
-                               "is int8 QK plus bf16 PV at both peaks, 3333 TOPS"},
+                               "is int8 QK plus bf16 PV at both nominal peaks, 3333 TOPS; the "
+                               "mixed sustained rate is the same blend of the sustained rates"},
             "rel_l1": {"ms": ms_rl1, "ms_median": median(2), "gbs": rl1_gbs,
                        "frac_hbm_peak": rl1_gbs / PEAK_HBM_GBS},
+            "step_ms": ms_step,
+            "mfma_sustained": sustained,
             "image_S4608": img,
+            "video_B2_S11440": vid,
             "fbcache_118800x3072": fbc,
             "quant_probe": probe,
             "fp8qk": fp8,
@@ -406,6 +535,7 @@ def main():
             "bf16_ex_bshd_bf16out_lse": ext,
             "wall_s_timed": wall,
         },
+        "env": env,
     }
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline()

@@ -17,6 +17,7 @@ Entry points (same names as the C ABI in include/ditattn.h):
   attn_quant_probe(q, k, v, o_q, n_rows=256, scale=None) -> err (fp32 [1 + B*H])
   fbcache_decide(resid, prev_resid, state, config, workspace=None) -> state
   resid_add(a, b, out=None) -> out;  resid_sub(a, b, out=None) -> out
+  mfma_probe(dtype, random_operands, iters) -> clocks   (calibration, not the attention path)
 
 plus helpers for the int8 workspace (int8qk_workspace, int8qk_views), the First Block Cache
 state (FBCacheConfig, fbcache_state, fbcache_state_values) and the library path.
@@ -40,7 +41,7 @@ __all__ = ["attn_fwd_bf16", "attn_fwd_int8qk", "attn_fwd_fp8qk", "attn_fwd_fp8",
            "int8qk_views", "int8qk_workspace_bytes", "rel_l1_workspace_bytes", "fbcache_decide",
            "resid_add", "resid_sub", "FBCacheConfig", "fbcache_state", "fbcache_state_values",
            "attn_quant_probe", "quant_probe_workspace_bytes", "quant_probe_views",
-           "lib", "LIB_PATH", "DitAttnError"]
+           "mfma_probe", "mfma_probe_flops", "lib", "LIB_PATH", "DitAttnError"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libditattn.so")
 
@@ -125,6 +126,8 @@ def declare(L: ctypes.CDLL) -> ctypes.CDLL:
     L.resid_add.restype = i
     L.resid_sub.argtypes = [vp, vp, vp, i64, vp]
     L.resid_sub.restype = i
+    L.ditattn_mfma_probe.argtypes = [i, i, i, vp, vp]
+    L.ditattn_mfma_probe.restype = i
     L.ditattn_status_string.argtypes = [i]
     L.ditattn_status_string.restype = ctypes.c_char_p
     return L
@@ -460,3 +463,26 @@ def resid_add(a, b, out=None):
 def resid_sub(a, b, out=None):
     """out = a - b over bf16 tensors, each value rounded once (out may be a or b)."""
     return _resid_op(lib().resid_sub, a, b, out)
+
+
+# ---- calibration (not part of the attention path) ------------------------------------------
+
+MFMA_PROBE_WORKGROUPS = 1024
+
+
+def mfma_probe_flops(dtype: str, iters: int) -> float:
+    """Work of one ditattn_mfma_probe launch: flops (bf16) or integer ops (int8)."""
+    per = 32 * 32 * (16 if dtype == "bf16" else 32) * 2
+    return float(MFMA_PROBE_WORKGROUPS) * 8 * iters * 8 * per
+
+
+def mfma_probe(dtype: str = "bf16", random_operands: bool = True, iters: int = 1000, clocks=None):
+    """Launch the matrix-core calibration kernel on the current stream; returns the int64
+    clocks tensor [1024, 2] (shader clocks, 100 MHz reference clocks per workgroup)."""
+    if dtype not in ("bf16", "int8"):
+        raise ValueError("dtype must be 'bf16' or 'int8'")
+    if clocks is None:
+        clocks = torch.empty((MFMA_PROBE_WORKGROUPS, 2), dtype=torch.int64, device="cuda")
+    _check(lib().ditattn_mfma_probe(0 if dtype == "bf16" else 1, 1 if random_operands else 0,
+                                    int(iters), _ptr(clocks), _stream(clocks)))
+    return clocks

@@ -11,6 +11,7 @@ that feature, which is harmless.
 from __future__ import annotations
 
 import glob
+import json
 import os
 import shutil
 import subprocess
@@ -23,6 +24,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libditattn.so")
+BUILD_INFO = os.path.join(PKG, "build_info.json")
 ARCH = "gfx950"
 
 FLAGS = [
@@ -61,7 +63,24 @@ def build(verbose: bool = False) -> str:
     tmp = LIB + ".tmp"
     _run([hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs])
     os.replace(tmp, LIB)
+    _write_build_info()
     return LIB
+
+
+def _write_build_info() -> None:
+    """Record which source revision the library was built from (the benchmark reports it; the
+    GPU machine that runs the benchmark has the built tree but not its git history)."""
+    def git(*args):
+        try:
+            r = subprocess.run(["git", "-C", ROOT, *args], capture_output=True, text=True, timeout=30)
+            return r.stdout.strip() if r.returncode == 0 else None
+        except (OSError, subprocess.SubprocessError):
+            return None
+    sha = git("rev-parse", "HEAD")
+    status = git("status", "--porcelain", "--untracked-files=no")
+    info = {"git_sha": sha, "dirty": bool(status) if status is not None else None}
+    with open(BUILD_INFO, "w") as f:
+        json.dump(info, f)
 
 
 if __name__ == "__main__":

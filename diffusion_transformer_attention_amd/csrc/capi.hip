@@ -366,6 +366,13 @@ int fbcache_decide(const void* resid, const void* prev_resid, int64_t n,
                                                   static_cast<hipStream_t>(stream)));
 }
 
+int ditattn_mfma_probe(int dtype, int random_operands, int iters, int64_t* clocks, void* stream) {
+  if ((dtype != 0 && dtype != 1) || (random_operands != 0 && random_operands != 1)) return DITATTN_EINVAL;
+  if (iters < 1 || !clocks || !aligned(clocks, 8)) return DITATTN_EINVAL;
+  return status_of(ditattn::launch_mfma_probe(dtype == 1, random_operands == 1, iters, clocks,
+                                              static_cast<hipStream_t>(stream)));
+}
+
 int resid_add(const void* a, const void* b, void* out, int64_t n, void* stream) {
   const int st = check_elementwise(a, b, out, n);
   if (st != DITATTN_OK) return st;

@@ -109,6 +109,13 @@ hipError_t launch_quant_probe(const AttnCall& base, const void* o_q, bool o_q_bf
                               int R, float* err, float* part, float* lse, double* sums,
                               hipStream_t stream);
 
+// Calibration (not part of the attention path): mfma_probe_workgroups() workgroups of 8
+// wavefronts, each issuing iters x 8 independent 32x32 products (bf16 or int8) on random or
+// constant operands; clocks[2 w], clocks[2 w + 1]: shader and 100 MHz reference clocks of
+// workgroup w.
+int mfma_probe_workgroups();
+hipError_t launch_mfma_probe(bool int8, bool random, int iters, int64_t* clocks, hipStream_t stream);
+
 // out = bf16(a + b) (SUB: a - b) elementwise over n bf16 values, each rounded once.
 hipError_t launch_resid_addsub(const void* a, const void* b, void* out, int64_t n, bool sub,
                                hipStream_t stream);

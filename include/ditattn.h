@@ -311,6 +311,25 @@ DITATTN_API int resid_sub(const void* a, const void* b, void* out, int64_t n, vo
 /* Static English description of a status code (never NULL). */
 DITATTN_API const char* ditattn_status_string(int status);
 
+/* ---- calibration (measurement support, not part of the attention path) ------------------
+ *
+ * For the callers that report attention throughput against the matrix cores' capability (the
+ * benchmark): the nominal dense peaks assume the rated clock, which a power-limited chip does
+ * not hold under dense products on real data.  ditattn_mfma_probe launches 1024 workgroups of
+ * 512 threads (8 wavefronts, two per SIMD on every CU of a 256-CU part, four rounds); every
+ * wavefront issues iters x 8 independent 32x32 matrix products back to back and nothing else:
+ *   dtype 0: v_mfma_f32_32x32x16_bf16 (32768 flops each); 1: v_mfma_i32_32x32x32_i8 (65536 ops)
+ *   random_operands 1: per-lane random operand values; 0: constant ones
+ *   iters  : >= 1
+ *   clocks : int64 device buffer of >= 2048 entries, caller owned: clocks[2 w] = shader clocks
+ *            workgroup w ran for, clocks[2 w + 1] = 100 MHz reference clocks over the same
+ *            interval (their ratio x 100 MHz is the shader clock it ran at)
+ * The caller times the launch on `stream`; the work is 1024 x 8 x iters x 8 products.
+ * DITATTN_EINVAL for other dtype / random_operands values, iters < 1 or a null or misaligned
+ * clocks pointer. */
+DITATTN_API int ditattn_mfma_probe(int dtype, int random_operands, int iters, int64_t* clocks,
+                                   void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -40,7 +40,7 @@ def test_header_declares_the_three_calls():
               "attn_quant_probe", "attn_fwd_fp8qk", "attn_fwd_fp8qk_ex", "attn_fwd_fp8",
               "attn_fwd_fp8_ex", "resid_rel_l1_noalloc"):
         assert n in names
-    assert len(names) == 22
+    assert len(names) == 23
 
 
 def test_library_exports_every_declared_symbol(L):
@@ -212,6 +212,15 @@ def test_rel_l1_noalloc_argument_errors(L):
     assert L.resid_rel_l1_noalloc(FAKE + 2, FAKE + 0x100, 100, FAKE + 0x1000, None) == EINVAL
     assert L.resid_rel_l1_noalloc(FAKE, FAKE + 0x108, 100, FAKE + 0x1000, None) == EINVAL
     assert L.resid_rel_l1_noalloc(FAKE, FAKE + 0x100, 100, FAKE + 0x1002, None) == EINVAL
+
+
+def test_mfma_probe_argument_errors(L):
+    assert L.ditattn_mfma_probe(2, 1, 10, FAKE, None) == EINVAL
+    assert L.ditattn_mfma_probe(-1, 1, 10, FAKE, None) == EINVAL
+    assert L.ditattn_mfma_probe(0, 2, 10, FAKE, None) == EINVAL
+    assert L.ditattn_mfma_probe(0, 1, 0, FAKE, None) == EINVAL
+    assert L.ditattn_mfma_probe(1, 0, 10, None, None) == EINVAL
+    assert L.ditattn_mfma_probe(1, 0, 10, FAKE + 4, None) == EINVAL
 
 
 def test_quant_probe_workspace_and_errors(L):
