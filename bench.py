@@ -264,9 +264,10 @@ def time_shape(torch, dta, stream, ev, B, H, S, D, iters, clock_khz, cus):
     the mean, then `iters` each between their own events for the median."""
     q, k, v = make_inputs(torch, B, H, S, D, seed=1)
     ws = dta.int8qk_workspace(B, H, S, D, "cuda")
+    ws16 = dta.bf16_workspace(B, H, S, D, "cuda")
     o = torch.empty((B, H, S, D), dtype=torch.float32, device="cuda")
     out = {}
-    for name, fn in (("bf16", lambda: dta.attn_fwd_bf16(q, k, v, out=o)),
+    for name, fn in (("bf16", lambda: dta.attn_fwd_bf16(q, k, v, out=o, workspace=ws16)),
                      ("int8qk", lambda: dta.attn_fwd_int8qk(q, k, v, out=o, workspace=ws))):
         for _ in range(5):
             fn()
@@ -288,7 +289,7 @@ def time_shape(torch, dta, stream, ev, B, H, S, D, iters, clock_khz, cus):
         rate = attn_flops(B, H, S, D) / (ms * 1e-3) / 1e12
         out[name] = {"ms": ms, "ms_median": per_call[iters // 2], "tflops": rate,
                      **_fracs(rate, "bf16" if name == "bf16" else "int8", clock_khz, cus)}
-    del q, k, v, ws, o
+    del q, k, v, ws, ws16, o
     torch.cuda.empty_cache()
     return out
 
@@ -349,7 +350,8 @@ def time_extended(torch, dta, stream, ev, q, k, v, iters=2):
     qs, ks, vs = (t.permute(0, 2, 1, 3).contiguous().transpose(1, 2) for t in (q, k, v))
     o = torch.empty((B, S, H, D), dtype=torch.bfloat16, device="cuda").transpose(1, 2)
     lse = torch.empty((B, H, S), dtype=torch.float32, device="cuda")
-    fn = lambda: dta.attn_fwd_bf16(qs, ks, vs, out=o, lse=lse)  # noqa: E731
+    ws16 = dta.bf16_workspace(B, H, S, D, "cuda")
+    fn = lambda: dta.attn_fwd_bf16(qs, ks, vs, out=o, lse=lse, workspace=ws16)  # noqa: E731
     fn()
     e0, e1 = ev(), ev()
     torch.cuda.synchronize()
@@ -427,6 +429,7 @@ def main():
     o_bf16 = torch.empty((B, H, S, D), dtype=torch.float32, device="cuda")
     o_int8 = torch.empty_like(o_bf16)
     ws8 = dta.int8qk_workspace(B, H, S, D, "cuda")
+    ws16 = dta.bf16_workspace(B, H, S, D, "cuda")
     r_out = torch.empty(1, dtype=torch.float32, device="cuda")
     ws_rl1 = torch.empty(dta.rel_l1_workspace_bytes(a.numel()), dtype=torch.uint8, device="cuda")
     torch.cuda.synchronize()
@@ -437,7 +440,7 @@ def main():
     def step(marks=None):
         if marks is not None:
             marks[0].record(stream)
-        dta.attn_fwd_bf16(q, k, v, out=o_bf16)
+        dta.attn_fwd_bf16(q, k, v, out=o_bf16, workspace=ws16)
         if marks is not None:
             marks[1].record(stream)
         dta.attn_fwd_int8qk(q, k, v, out=o_int8, workspace=ws8)

@@ -8,7 +8,7 @@ raises.
 
 Entry points (same names as the C ABI in include/ditattn.h):
 
-  attn_fwd_bf16(q, k, v, out=None, scale=None) -> out
+  attn_fwd_bf16(q, k, v, out=None, scale=None, workspace=None) -> out
   attn_fwd_int8qk(q, k, v, out=None, scale=None, workspace=None) -> out
   attn_fwd_fp8qk(q, k, v, out=None, scale=None, workspace=None) -> out
   attn_fwd_fp8(q, k, v, out=None, scale=None, workspace=None) -> out   (fp8 QK and PV, D = 128)
@@ -19,14 +19,16 @@ Entry points (same names as the C ABI in include/ditattn.h):
   resid_add(a, b, out=None) -> out;  resid_sub(a, b, out=None) -> out
   mfma_probe(dtype, random_operands, iters) -> clocks   (calibration, not the attention path)
 
-plus helpers for the int8 workspace (int8qk_workspace, int8qk_views), the First Block Cache
-state (FBCacheConfig, fbcache_state, fbcache_state_values) and the library path.
+plus helpers for the workspaces (bf16_workspace, int8qk_workspace, int8qk_views), the First
+Block Cache state (FBCacheConfig, fbcache_state, fbcache_state_values) and the library path.
 
 The attention calls also take strided [B, H, S, D] views (channel axis contiguous), for
 instance q.transpose(1, 2) of a [B, S, H, D] tensor or a slice of a fused QKV projection, an
 output dtype (out_dtype=torch.bfloat16, or a bf16 `out`) and `lse` (a fp32 [B, H, S] tensor,
 or lse=True to allocate one), which return (out, lse); those go through the C ABI's
 attn_fwd_bf16_ex / attn_fwd_int8qk_ex, the plain contiguous fp32 case through the plain calls.
+With a workspace (the default) the bf16 call goes through attn_fwd_bf16_ws, which shares the
+last, partly filled round of query tiles out over every CU.
 """
 from __future__ import annotations
 
@@ -36,7 +38,7 @@ import os
 
 import torch  # loaded first: the library then binds to the HIP runtime torch already holds
 
-__all__ = ["attn_fwd_bf16", "attn_fwd_int8qk", "attn_fwd_fp8qk", "attn_fwd_fp8", "fp8_workspace",
+__all__ = ["attn_fwd_bf16", "bf16_workspace", "bf16_workspace_bytes", "attn_fwd_int8qk", "attn_fwd_fp8qk", "attn_fwd_fp8", "fp8_workspace",
            "fp8_views", "resid_rel_l1", "resid_rel_l1_noalloc", "int8qk_workspace",
            "int8qk_views", "int8qk_workspace_bytes", "rel_l1_workspace_bytes", "fbcache_decide",
            "resid_add", "resid_sub", "FBCacheConfig", "fbcache_state", "fbcache_state_values",
@@ -106,6 +108,10 @@ def declare(L: ctypes.CDLL) -> ctypes.CDLL:
     L.attn_fwd_fp8qk_ex.restype = i
     L.attn_fwd_bf16_ex.argtypes = [vp, vp, vp, vp, i, vp, p64, i, i, i, i, f, vp]
     L.attn_fwd_bf16_ex.restype = i
+    L.attn_bf16_workspace_bytes.argtypes = [i, i, i, i]
+    L.attn_bf16_workspace_bytes.restype = sz
+    L.attn_fwd_bf16_ws.argtypes = [vp, vp, vp, vp, i, vp, p64, i, i, i, i, f, vp, sz, vp]
+    L.attn_fwd_bf16_ws.restype = i
     L.attn_fwd_int8qk_ex.argtypes = [vp, vp, vp, vp, i, vp, p64, i, i, i, i, f, vp, sz, vp]
     L.attn_fwd_int8qk_ex.restype = i
     L.resid_rel_l1_workspace_bytes.argtypes = [i64]
@@ -201,13 +207,37 @@ def _strides_arg(q, k, v, out):
                                    + _bhs_strides(out)))
 
 
-def attn_fwd_bf16(q, k, v, out=None, scale=None, *, out_dtype=None, lse=None):
+def bf16_workspace_bytes(B, H, S, D) -> int:
+    return int(lib().attn_bf16_workspace_bytes(B, H, S, D))
+
+
+def bf16_workspace(B, H, S, D, device) -> torch.Tensor:
+    """A uint8 device buffer large enough for attn_fwd_bf16's split of the last round."""
+    n = bf16_workspace_bytes(B, H, S, D)
+    if n == 0:
+        raise DitAttnError(-1, "invalid shape")
+    return torch.empty(n, dtype=torch.uint8, device=device)
+
+
+def attn_fwd_bf16(q, k, v, out=None, scale=None, *, out_dtype=None, lse=None, workspace=None):
     """Exact attention O = softmax(Q K^T * scale) V on bf16 [B,H,S,D] views.
 
+    workspace: a bf16_workspace buffer, None to allocate one, or False for the calls that take
+    none (whole tiles only: the last round of query tiles may leave CUs idle).
     Returns out (fp32 unless out_dtype / out say bf16), or (out, lse) when lse is given."""
     (B, H, S, D), out, lse_t, plain = _attn_args(q, k, v, out, out_dtype, lse)
     scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
-    if plain:
+    if workspace is not False:
+        if workspace is None:
+            workspace = bf16_workspace(B, H, S, D, q.device)
+        if workspace.dtype != torch.uint8 or not workspace.is_cuda or not workspace.is_contiguous():
+            raise ValueError("workspace must be a contiguous uint8 CUDA tensor")
+        _check(lib().attn_fwd_bf16_ws(
+            _ptr(q), _ptr(k), _ptr(v), _ptr(out),
+            OUT_BF16 if out.dtype == torch.bfloat16 else OUT_F32, _ptr(lse_t),
+            _strides_arg(q, k, v, out), B, H, S, D, scale, _ptr(workspace), workspace.numel(),
+            _stream(q)))
+    elif plain:
         _check(lib().attn_fwd_bf16(_ptr(q), _ptr(k), _ptr(v), _ptr(out), B, H, S, D, scale,
                                    _stream(q)))
     else:

@@ -4,6 +4,8 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <algorithm>
+
 #include "ditattn.h"
 #include "kernels.h"
 
@@ -81,6 +83,7 @@ ditattn::AttnCall make_call(const void* q, const void* k, const void* v, void* o
   ac.os = {st[9], st[10], st[11]};
   ac.B = B; ac.H = H; ac.S = S; ac.D = D; ac.scale = scale;
   ac.Sq = S;
+  ac.tail = nullptr;
   return ac;
 }
 
@@ -95,7 +98,7 @@ void contiguous_strides(int H, int S, int D, int64_t st[12]) {
 enum Q8Mode { kQ8Int8, kQ8Fp8Qk, kQ8Fp8All };
 
 // The int8 / fp8 paths after validation: workspace check, prepass, attention.
-int q8_run(const ditattn::AttnCall& ac, Q8Mode mode, void* workspace, size_t workspace_bytes,
+int q8_run(ditattn::AttnCall ac, Q8Mode mode, void* workspace, size_t workspace_bytes,
            hipStream_t s) {
   if (mode == kQ8Fp8All && ac.D != 128) return DITATTN_EUNSUPPORTED;
   const bool fp8 = mode != kQ8Int8;
@@ -110,6 +113,8 @@ int q8_run(const ditattn::AttnCall& ac, Q8Mode mode, void* workspace, size_t wor
   int8_t* q_codes = reinterpret_cast<int8_t*>(ws + off[3]);
   int8_t* k_codes = reinterpret_cast<int8_t*>(ws + off[4]);
   double* partial = reinterpret_cast<double*>(ws + off[5]);
+  // the scratch segment serves the attention launch too, after the prepass is done with it
+  if (ditattn::attn_tail_bytes(ac.S, ac.D) > 0) ac.tail = ws + off[5];
   const hipError_t e = ditattn::launch_prepass(ac.q, ac.qs, ac.k, ac.ks, k_mean, partial, q_codes,
                                                k_codes, q_scale, k_scale, ac.B, ac.H, ac.S, ac.D,
                                                fp8, s);
@@ -182,6 +187,25 @@ int attn_fwd_bf16_ex(const void* q, const void* k, const void* v, void* o, int o
       static_cast<hipStream_t>(stream)));
 }
 
+size_t attn_bf16_workspace_bytes(int B, int H, int S, int D) {
+  if (check_attn_shape(B, H, S, D) != DITATTN_OK) return 0;
+  return std::max(ditattn::attn_tail_bytes(S, D), kSegAlign);
+}
+
+int attn_fwd_bf16_ws(const void* q, const void* k, const void* v, void* o, int out_dtype,
+                     float* lse, const int64_t* strides, int B, int H, int S, int D, float scale,
+                     void* workspace, size_t workspace_bytes, void* stream) {
+  const int st = check_ex_args(q, k, v, o, out_dtype, lse, strides, B, H, S, D, scale);
+  if (st != DITATTN_OK) return st;
+  if (!workspace || !aligned(workspace, kSegAlign) ||
+      workspace_bytes < attn_bf16_workspace_bytes(B, H, S, D))
+    return DITATTN_EWORKSPACE;
+  ditattn::AttnCall ac =
+      make_call(q, k, v, o, out_dtype == DITATTN_OUT_BF16, lse, strides, B, H, S, D, scale);
+  if (ditattn::attn_tail_bytes(S, D) > 0) ac.tail = workspace;
+  return status_of(ditattn::launch_attn_bf16(ac, static_cast<hipStream_t>(stream)));
+}
+
 size_t attn_int8qk_workspace_offsets(int B, int H, int S, int D, size_t offsets[6]) {
   if (check_attn_shape(B, H, S, D) != DITATTN_OK) return 0;
   const size_t bh = (size_t)B * (size_t)H;
@@ -191,7 +215,9 @@ size_t attn_int8qk_workspace_offsets(int B, int H, int S, int D, size_t offsets[
       bh * (size_t)((S + 63) / 64) * sizeof(float),         // k_scale
       bh * (size_t)S * D,                                   // q_codes
       bh * (size_t)S * D,                                   // k_codes
-      bh * (size_t)ditattn::kmean_chunks(B, H, S) * D * 2 * sizeof(double),  // mean partials
+      // mean partials, then (once the codes are formed) the attention's tail workspace
+      std::max(bh * (size_t)ditattn::kmean_chunks(B, H, S) * D * 2 * sizeof(double),
+               ditattn::attn_tail_bytes(S, D)),
   };
   size_t off = 0;
   for (int i = 0; i < 6; ++i) {

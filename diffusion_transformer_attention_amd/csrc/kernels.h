@@ -31,7 +31,14 @@ struct AttnCall {
   int B, H, S, D;
   float scale;
   int Sq;
+  // attn_tail_bytes(S, D) bytes of device memory (256-byte aligned) in which the launch shares
+  // its last, partly filled round of query tiles out over every CU; null: whole tiles only.
+  void* tail;
 };
+
+// Bytes of the tail workspace of an attention launch over S keys (0 when no launch over S keys
+// can have a tail phase).
+size_t attn_tail_bytes(int S, int D);
 
 hipError_t launch_attn_bf16(const AttnCall& ac, hipStream_t stream);
 

@@ -77,7 +77,8 @@ DITATTN_API int attn_fwd_bf16(const void* q, const void* k, const void* v, float
  *   [2] k_scale fp32 [B, H, ceil(S/64)]   one scale per 64-token block of smoothed K
  *   [3] q_codes int8 [B, H, S, D]
  *   [4] k_codes int8 [B, H, S, D]
- *   [5] scratch  fp64 pairs used while forming k_mean (contents unspecified)
+ *   [5] scratch  fp64 pairs used while forming k_mean, then the attention's tail workspace
+ *                (see attn_fwd_bf16_ws; contents unspecified)
  * After a successful call segments [0]-[4] hold the values the attention used. */
 DITATTN_API size_t attn_int8qk_workspace_bytes(int B, int H, int S, int D);
 
@@ -168,6 +169,26 @@ DITATTN_API int attn_fwd_fp8(const void* q, const void* k, const void* v, float*
 DITATTN_API int attn_fwd_bf16_ex(const void* q, const void* k, const void* v, void* o,
                                  int out_dtype, float* lse, const int64_t* strides,
                                  int B, int H, int S, int D, float scale, void* stream);
+
+/* As attn_fwd_bf16_ex, with a workspace that lets the call share its last round of query
+ * tiles out over every CU.  The calls above run one workgroup (one CU) per tile of 256 query
+ * rows of one (b, h); when the B * H * ceil(S / 256) tiles are not a multiple of the CU count
+ * the last round leaves CUs idle (1024^2 images, B1 H24 S4608: 432 tiles on 256 CUs).  Here
+ * the tiles of that last round are cut along the key axis into equal ranges, one per CU, and
+ * the partial results of a tile are merged exactly as the extended calls describe (running
+ * maximum and sum: the online softmax of the "Flash Attention 2 for Z-Image S3-DiT" page,
+ * method paragraph, applied across parts), in a fixed order, so the output does not depend on
+ * timing.  Tiles of the full rounds are computed exactly as attn_fwd_bf16 computes them; in
+ * the last round each tile's sums over the keys are formed in parts and then merged.
+ *   workspace : device buffer of >= attn_bf16_workspace_bytes(B, H, S, D) bytes, 256-byte
+ *               aligned, caller owned, contents unspecified before and after; calls that use
+ *               one workspace at the same time (on different streams) race
+ * Errors as attn_fwd_bf16_ex, plus DITATTN_EWORKSPACE. */
+DITATTN_API size_t attn_bf16_workspace_bytes(int B, int H, int S, int D);
+DITATTN_API int attn_fwd_bf16_ws(const void* q, const void* k, const void* v, void* o,
+                                 int out_dtype, float* lse, const int64_t* strides,
+                                 int B, int H, int S, int D, float scale,
+                                 void* workspace, size_t workspace_bytes, void* stream);
 
 /* As attn_fwd_int8qk with the additions above; the workspace (size and layout) is the same,
  * its codes stay contiguous [B, H, S, D] whatever the strides of q and k. */

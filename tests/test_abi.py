@@ -38,9 +38,10 @@ def test_header_declares_the_three_calls():
     for n in ("attn_fwd_bf16", "attn_fwd_int8qk", "resid_rel_l1", "attn_fwd_bf16_ex",
               "attn_fwd_int8qk_ex", "fbcache_decide", "resid_add", "resid_sub",
               "attn_quant_probe", "attn_fwd_fp8qk", "attn_fwd_fp8qk_ex", "attn_fwd_fp8",
-              "attn_fwd_fp8_ex", "resid_rel_l1_noalloc"):
+              "attn_fwd_fp8_ex", "resid_rel_l1_noalloc", "attn_fwd_bf16_ws",
+              "attn_bf16_workspace_bytes"):
         assert n in names
-    assert len(names) == 23
+    assert len(names) == 25
 
 
 def test_library_exports_every_declared_symbol(L):
@@ -70,6 +71,8 @@ def test_int8_workspace_layout(L, B, H, S, D):
         assert off[i] == expect and off[i] % 256 == 0
         expect = _align(expect + sz)
     assert off[5] == expect and total > off[5] and total % 256 == 0
+    # the scratch segment also holds the attention's tail workspace
+    assert total - off[5] >= _tail_bytes(S, D)
 
 
 @pytest.mark.parametrize("B,H,S,D", [(1, 2, 256, 128), (1, 24, 118800, 128), (3, 1, 1, 128)])
@@ -97,6 +100,40 @@ def test_fp8_all_argument_errors(L):
     st = (ctypes.c_int64 * 12)(*_contig(1, 64, 128))
     assert L.attn_fwd_fp8_ex(FAKE, FAKE + 0x1000, FAKE + 0x2000, FAKE + 0x3000, 5, None, st, 1, 1,
                              64, 128, 0.125, FAKE + 0x8000, need, None) == EINVAL
+
+
+def _tail_bytes(S, D):
+    """The split of the last round: 256 counters (1 KB), then 2 slots for each of up to 256
+    workgroups, a slot holding 512 lanes x (D/2 O values + m + l) fp32; none for 8 key tiles or
+    fewer (ranges of 8 key tiles, each shorter than a tile)."""
+    if math.ceil(S / 64) <= 8:
+        return 0
+    return 1024 + 2 * 256 * 512 * (D // 2 + 2) * 4
+
+
+@pytest.mark.parametrize("S", [1, 64, 448, 449, 512, 4608, 11440, 118800])
+@pytest.mark.parametrize("D", [64, 128])
+def test_bf16_workspace_size(L, S, D):
+    assert L.attn_bf16_workspace_bytes(1, 24, S, D) == max(_tail_bytes(S, D), 256)
+    assert L.attn_bf16_workspace_bytes(1, 24, S, 96) == 0
+    assert L.attn_bf16_workspace_bytes(0, 24, S, D) == 0
+
+
+def test_bf16_ws_argument_errors(L):
+    st = (ctypes.c_int64 * 12)(*_contig(1, 4608, 128))
+    need = L.attn_bf16_workspace_bytes(1, 1, 4608, 128)
+    args = [FAKE, FAKE + 0x1000, FAKE + 0x2000, FAKE + 0x3000, 0, None, st, 1, 1, 4608, 128, 0.125]
+    assert L.attn_fwd_bf16_ws(*args, None, need, None) == EWS
+    assert L.attn_fwd_bf16_ws(*args, FAKE + 0x8000, need - 1, None) == EWS
+    assert L.attn_fwd_bf16_ws(*args, FAKE + 0x8010, need, None) == EWS   # not 256-aligned
+    bad = list(args); bad[4] = 7                                          # out_dtype
+    assert L.attn_fwd_bf16_ws(*bad, FAKE + 0x8000, need, None) == EINVAL
+    bad = list(args); bad[6] = None                                       # strides
+    assert L.attn_fwd_bf16_ws(*bad, FAKE + 0x8000, need, None) == EINVAL
+    bad = list(args); bad[10] = 96
+    assert L.attn_fwd_bf16_ws(*bad, FAKE + 0x8000, need, None) == EUNSUP
+    bad = list(args); bad[3] = FAKE                                       # o aliases q
+    assert L.attn_fwd_bf16_ws(*bad, FAKE + 0x8000, need, None) == EINVAL
 
 
 def test_invalid_shapes_give_zero_workspace(L):
