@@ -1,7 +1,7 @@
 """Benchmark of the DiT attention hot path on one MI355X.
 
 One step = the whole path once over one batch of resident synthetic input:
-  attn_fwd_bf16    B=1 H=24 S=118800 D=128 (a 720p 129-frame video latent)
+  attn_fwd_bf16    B=1 H=24 S=118800 D=128 (a 720p 129-frame video latent), on its workspace
   attn_fwd_int8qk  same tensors (K mean, int8 quantization and int8-QK attention)
   resid_rel_l1     two bf16 [118800, 3072] first-block residuals
 Throughput counts 4*B*H*S^2*D flops per attention call.  `value` is the bf16 call's TFLOP/s
@@ -41,7 +41,11 @@ SUSTAINED = {}
 # The int8-QK call does half its counted flops (QK) on int8 MFMA and half (PV) on bf16 MFMA, so
 # even at both peaks it reaches only 1 / (0.5 / 5000 + 0.5 / 2500) = 3333 TOPS (66.7% of int8).
 PEAK_INT8_BF16PV_TOPS = 1.0 / (0.5 / PEAK_INT8_TOPS + 0.5 / PEAK_BF16_TFLOPS)
-ATTN_KERNEL = "attn_fwd_kernel<128, 0, 8>"
+# The bf16 call on its workspace is two launches of one kernel template: the 43 whole rounds of
+# 256-row query tiles and the last 152 tiles shared out over the CUs.  The roofline covers the
+# call (both launches): its flops over its HIP-event time, its counters summed.
+ATTN_KERNEL = ("attn_fwd_kernel<128, 0, 8, false> + attn_fwd_kernel<128, 0, 8, true> "
+               "(one attn_fwd_bf16_ws call: whole rounds, then the shared-out last round)")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_bf16_longvideo_traffic.json")
 
 
