@@ -653,7 +653,7 @@ void attn_fwd_kernel(const uint8_t* __restrict__ qp, const uint8_t* __restrict__
     // 4-byte steps moved the long-video int8 call by up to 3% (shifts that are a multiple of 8
     // bytes from the unpadded placement were the slow ones) and the bf16 call by up to 1%.
     // These pads are the measured best for this loop and compiler.
-    pad_nops<KIND == kInt8 ? 1 : 3>();
+    pad_nops<KIND == kInt8 ? 2 : 3>();
 
     // stage j reads S[j+1] and writes S[j+2]; consumes P[j] and produces P[j+1]
     int j = kbeg;
