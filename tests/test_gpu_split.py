@@ -7,7 +7,8 @@ partial results in key order (csrc/split_plan.h).  Checked here:
 
 * parity with the oracle on every row of shapes whose tail tiles have three or four parts and
   whose workgroups hold two segments (ragged key and query lengths, D = 64 and 128), on the
-  bf16, int8-QK and fp8-QK paths, with the tolerances of test_gpu_parity.py;
+  bf16, int8-QK and fp8-QK paths, with the tolerances of test_gpu_parity.py, and of fp8 for
+  both products against the error model and ceiling of test_gpu_fp8.py;
 * strided views, bf16 output and the log-sum-exp through the split;
 * the result does not depend on which part arrives last: repeated calls are bit-identical,
   also from a workspace filled with garbage, and the arrival counters are left at zero;
@@ -159,3 +160,23 @@ def test_split_deterministic_from_garbage_workspace():
     r = float((a - whole).norm() / whole.norm())
     announce(f"  repeated calls bit-identical; split vs whole tiles rel-L2 {r:.3e}")
     assert r <= 2e-3, r
+
+
+def test_split_fp8_both_products():
+    """fp8 for both products through the split (D = 128): each part rounds its weights to e4m3
+    at its own running offset, so the output is held to the fp8-PV error model and ceiling of
+    tests/test_gpu_fp8.py against the oracle, not to the element-wise bar."""
+    from test_gpu_fp8 import check_out_model, fp8_pv_error_model
+    B, H, S, D = 1, 5, 4000, 128
+    n_main, n_tail, nkt = tail_plan(B, H, S)
+    announce(f"attn_fwd_fp8 B{B} H{H} S{S} D{D}: {n_tail} split tiles")
+    assert n_tail > 0
+    q, k, v = inputs(B, H, S, D, 1050)
+    ws = dta.fp8_workspace(B, H, S, D, "cuda")
+    got = dta.attn_fwd_fp8(dev(q), dev(k), dev(v), workspace=ws).cpu().numpy()
+    ref = oracle.quantize_qk_fp8(f64(q), f64(k))
+    vc, vs = oracle.quantize_v_fp8(f64(v))
+    oq = oracle.attention_fp8_full(ref["q_codes"], ref["q_scale"], ref["k_codes"], ref["k_scale"], vc, vs)
+    vq = oracle.e4m3_value(vc) * vs[:, :, None, :]
+    check_out_model(got, oq, oracle.attention(f64(q), f64(k), f64(v)), fp8_pv_error_model(ref, vq),
+                    "fp8 QK and PV, split")
