@@ -68,6 +68,12 @@ constexpr int kBK = 64;         // keys per tile (= int8 K block)
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kLazyW = 256.0f;  // 2^8: largest weight (and lane weight sum) kept as it is
+// bf16 calls over at least this many keys (D = 128, with a workspace) read V through V^T tiles
+// written by a prepass: one 16-byte LDS read per PV operand instead of two transposing ones,
+// 1-1.6% faster at S = 118800 with the prepass (a read and a write of V) included.  The
+// prepass costs 2% of the call at S = 11440, as much as the tiles save; on the int8-QK kernel
+// the tiles gain nothing.
+constexpr int kVtMinS = 32768;
 // fp8 weights are formed 2^4 times larger (the small ones then fall in e4m3's normal range, not
 // its coarse subnormals), and kept while their lane sum is <= 2^8, so every one is <= 256 < 448.
 constexpr float kLog2WScale8 = 4.0f;
@@ -174,7 +180,8 @@ struct KArgs {
 // the design and a third wave slot could not hold a second workgroup, yet aiming for three
 // squeezes the kernel into 168 VGPRs and serialises its K fragment reads behind the products.
 // (At D = 128 the cap changes nothing but the instruction schedule, measurably for the worse.)
-template <int D, int KIND, int NW, bool TAIL>
+// VT: vp holds the V^T tiles of vt_tiles_kernel (bf16 path, D = 128) instead of V itself.
+template <int D, int KIND, int NW, bool TAIL, bool VT>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, D == 64 ? 2 : 8)))
 void attn_fwd_kernel(const uint8_t* __restrict__ qp, const uint8_t* __restrict__ kp,
                      const uint8_t* __restrict__ vp, uint8_t* __restrict__ op,
@@ -188,6 +195,7 @@ void attn_fwd_kernel(const uint8_t* __restrict__ qp, const uint8_t* __restrict__
   constexpr bool F8 = KIND == kFp8 || KIND == kFp8All;
   constexpr bool V8 = KIND == kFp8All;  // fp8 V codes, PV on the fp8 matrix cores
   static_assert(!V8 || D == 128, "fp8 V is laid out for D = 128");
+  static_assert(!VT || (D == 128 && KIND == kBF16), "V^T tiles: bf16 path, D = 128");
   using T = Tile<D, INT8, NW, V8>;
   constexpr int EBV = V8 ? 1 : 2;       // bytes per V element
   constexpr int kThreads = T::NT;
@@ -240,7 +248,8 @@ void attn_fwd_kernel(const uint8_t* __restrict__ qp, const uint8_t* __restrict__
 
     const int bb = bh / a.H, hd = bh - bb * a.H;
     const uint8_t* kh = kp + (bb * a.ksb + hd * a.ksh) * EB;   // first key row of this (b, h)
-    const uint8_t* vh = vp + (bb * a.vsb + hd * a.vsh) * EBV;
+    // (V^T tiles: nkt contiguous tiles per (b, h))
+    const uint8_t* vh = VT ? vp + (size_t)bh * nkt * T::VBYTES : vp + (bb * a.vsb + hd * a.vsh) * EBV;
     const int64_t krs = a.kss * EB, vrs = a.vss * EBV;          // bytes between key / value rows
 
     // ---- Q fragment: B operand; lane holds query q, bytes [32f + 16hh, +16) of its row -------
@@ -291,8 +300,14 @@ void attn_fwd_kernel(const uint8_t* __restrict__ qp, const uint8_t* __restrict__
 #pragma unroll
     for (int r = 0; r < T::VLD; ++r) {
       const int p = r * kThreads + tid;
-      const int key = p / T::VCH, pch = p % T::VCH;
-      vofl[r] = (uint32_t)(key * vrs) + (V8 ? vswz8(key, pch) : vswz<D>(key, pch)) * 16;
+      if constexpr (VT) {
+        // a V^T tile: 128 channel rows of 64 keys (128 bytes), swizzled as an int8 K tile
+        const int row = p / 8, pch = p % 8;
+        vofl[r] = (uint32_t)(row * 128) + kswz<128, true>(row, pch) * 16;
+      } else {
+        const int key = p / T::VCH, pch = p % T::VCH;
+        vofl[r] = (uint32_t)(key * vrs) + (V8 ? vswz8(key, pch) : vswz<D>(key, pch)) * 16;
+      }
     }
     // The tile copies are buffer loads with the LDS as destination (MUBUF), on a buffer resource
     // whose base is the tile's first row and whose range covers every 32-bit offset.  The
@@ -308,11 +323,12 @@ void attn_fwd_kernel(const uint8_t* __restrict__ qp, const uint8_t* __restrict__
     // First row of tile kt: kt * kBK, except a ragged last tile, which starts at Sk - kBK
     // (Sk >= kBK whenever more than one tile exists).  Tiles of K and of V are each loaded once,
     // in order from kbeg, so their base addresses advance by one tile per load (uniform, in SGPRs).
-    const int64_t k_step = kBK * krs, v_step = kBK * vrs;
+    const int64_t k_step = kBK * krs, v_step = VT ? (int64_t)T::VBYTES : kBK * vrs;
     const uint8_t* k_next = kh + kbeg * k_step;
     const uint8_t* v_next = vh + kbeg * v_step;
     const uint8_t* const k_last = kh + (int64_t)max(Sk - kBK, 0) * krs;
-    const uint8_t* const v_last = vh + (int64_t)max(Sk - kBK, 0) * vrs;
+    const uint8_t* const v_last =
+        VT ? vh + (int64_t)(nkt - 1) * T::VBYTES : vh + (int64_t)max(Sk - kBK, 0) * vrs;
     // The offsets are redefined (by an empty asm) at the top of every loop iteration, so their
     // zero extension cannot be hoisted out of the loop and each address is selected as scalar
     // base + 32-bit vector offset (the global "saddr" form), not a 64-bit VALU add.
@@ -353,7 +369,8 @@ void attn_fwd_kernel(const uint8_t* __restrict__ qp, const uint8_t* __restrict__
         const int p = r * kThreads + tid;
         const int key = p / T::VCH, pch = p % T::VCH;
         const uint32_t off =
-            (uint32_t)(min(key, Sk - 1) * vrs) + (V8 ? vswz8(key, pch) : vswz<D>(key, pch)) * 16;
+            VT ? vofl[r]  // a V^T tile is always whole (its rows past Sk are zeros)
+               : (uint32_t)(min(key, Sk - 1) * vrs) + (V8 ? vswz8(key, pch) : vswz<D>(key, pch)) * 16;
         tile_dma(vh, off, vdst + (r * kThreads + wave_u * 64) * 16);
       }
     };
@@ -386,6 +403,14 @@ void attn_fwd_kernel(const uint8_t* __restrict__ qp, const uint8_t* __restrict__
         const int col = 32 * db + 16 * ((lane >> 4) & 1) + 4 * (gj & 3);
         voffs[db] = vrow * T::VROW + vswz<D>(vrow, col >> 3) * 16 + (col & 7) * 2;
       }
+    }
+
+    // V^T (VT): lane reads channel row 32 db + l32, logical chunk 2 c4 + hh (the 8 keys of its
+    // half of 16-key step c4, stored in P^T order); the swizzle does not depend on db.
+    int vtoffs[VT ? 4 : 1];
+    if constexpr (VT) {
+#pragma unroll
+      for (int c4 = 0; c4 < 4; ++c4) vtoffs[c4] = l32 * 128 + kswz<128, true>(l32, 2 * c4 + hh) * 16;
     }
 
     f32x16 oacc[T::NDB];
@@ -608,11 +633,16 @@ void attn_fwd_kernel(const uint8_t* __restrict__ qp, const uint8_t* __restrict__
       for (int c4 = 0; c4 < 4; ++c4) {
 #pragma unroll
         for (int db = 0; db < T::NDB; ++db) {
-          const uint8_t* base = vb_cur + voffs[db] + 16 * c4 * T::VROW;
-          const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(base));
-          const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(base + 8 * T::VROW));
-          const u32x2 lo2 = __builtin_bit_cast(u32x2, lo), hi2 = __builtin_bit_cast(u32x2, hi);
-          const u32x4 a = {lo2[0], lo2[1], hi2[0], hi2[1]};
+          u32x4 a;
+          if constexpr (VT) {
+            a = *reinterpret_cast<const u32x4*>(vb_cur + vtoffs[c4] + db * 32 * 128);
+          } else {
+            const uint8_t* base = vb_cur + voffs[db] + 16 * c4 * T::VROW;
+            const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(base));
+            const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(base + 8 * T::VROW));
+            const u32x2 lo2 = __builtin_bit_cast(u32x2, lo), hi2 = __builtin_bit_cast(u32x2, hi);
+            a = u32x4{lo2[0], lo2[1], hi2[0], hi2[1]};
+          }
           oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), p0[c4],
                                                              oacc[db], 0, 0, 0);
         }
@@ -656,7 +686,7 @@ void attn_fwd_kernel(const uint8_t* __restrict__ qp, const uint8_t* __restrict__
     // 4-byte steps moved the long-video int8 call by up to 3% (shifts that are a multiple of 8
     // bytes from the unpadded placement were the slow ones) and the bf16 call by up to 1%.
     // These pads are the measured best for this loop and compiler.
-    pad_nops<KIND == kInt8 ? 2 : 3>();
+    pad_nops<KIND == kInt8 ? 2 : VT ? 0 : 3>();
 
     // stage j reads S[j+1] and writes S[j+2]; consumes P[j] and produces P[j+1]
     int j = kbeg;
@@ -838,6 +868,53 @@ __global__ void zero_counters_kernel(int* __restrict__ c, int n) {
   for (int i = threadIdx.x; i < n; i += blockDim.x) c[i] = 0;
 }
 
+// Position p of a 16-key step in a V^T row holds key vt_key(p): keys 0-3, 8-11, 4-7, 12-15,
+// the order of the weights in the P^T operand (bits 2 and 3 swapped; an involution).
+__device__ __forceinline__ int vt_key(int p) { return (p & ~12) | ((p & 4) << 1) | ((p & 8) >> 1); }
+
+// V^T tiles of bf16 V at D = 128, for long sequences: tile t of (b, h) = bh holds the 64 keys
+// the attention's key tile t covers (the last one the final 64 rows, as its K tile) as 128
+// channel rows of 64 keys, vt[((bh * nkt + t) * 128 + channel) * 64 + position], each 16-key
+// step in P^T order (vt_key), so that one 16-byte LDS read gives a lane the 8 keys of its half
+// of a step; rows past S (only when S < 64) are zeros.  One workgroup per tile, through LDS.
+__global__ __launch_bounds__(256) void vt_tiles_kernel(const uint16_t* __restrict__ v, Strides vs,
+                                                        int H, int S, int nkt,
+                                                        uint16_t* __restrict__ vt) {
+  // 64 rows of 128 channels; the row pitch of 65 words puts the 8 rows a column read touches
+  // in 8 distinct banks
+  __shared__ uint32_t sm[64 * 65];
+  const int bh = blockIdx.x / nkt, t = blockIdx.x - bh * nkt;
+  const int r0 = t == nkt - 1 ? max(S - kBK, 0) : t * kBK;
+  const uint16_t* vh = v + (bh / H) * vs.b + (bh % H) * vs.h;
+  const int tid = threadIdx.x;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int c = tid + 256 * i;  // 16-byte chunk: row c / 16, channels 8 (c % 16) .. + 7
+    const int row = c >> 4, ch8 = (c & 15) * 8;
+    u32x4 x = u32x4{0u, 0u, 0u, 0u};
+    if (r0 + row < S) x = *reinterpret_cast<const u32x4*>(vh + (int64_t)(r0 + row) * vs.s + ch8);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) sm[row * 65 + ch8 / 2 + e] = x[e];
+  }
+  __syncthreads();
+  uint16_t* out = vt + ((size_t)bh * nkt + t) * 128 * kBK;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int c = tid + 256 * i;  // output chunk: channel c / 8, positions 8 (c % 8) .. + 7
+    const int ch = c >> 3, q = c & 7;
+    uint32_t w[4];
+#pragma unroll
+    for (int e = 0; e < 8; e += 2) {
+      const int p0 = 8 * q + e;
+      const int k0 = (p0 & ~15) | vt_key(p0 & 15), k1 = (p0 & ~15) | vt_key((p0 + 1) & 15);
+      const uint32_t a0 = sm[k0 * 65 + ch / 2] >> (16 * (ch & 1));
+      const uint32_t a1 = sm[k1 * 65 + ch / 2] >> (16 * (ch & 1));
+      w[e / 2] = (a0 & 0xFFFFu) | (a1 << 16);
+    }
+    *reinterpret_cast<u32x4*>(out + ch * kBK + 8 * q) = u32x4{w[0], w[1], w[2], w[3]};
+  }
+}
+
 // Workgroups of the attention kernel resident at once on the stream's device: one per CU
 // (8 wavefronts of two per SIMD), at most kTailMaxG.  Looked up once per device.
 hipError_t resident_workgroups(hipStream_t stream, int& G) {
@@ -896,18 +973,38 @@ hipError_t launch(const AttnCall& ac, const void* q, Strides qs, const void* k, 
   const uint8_t* kb = static_cast<const uint8_t*>(k);
   const uint8_t* vb = static_cast<const uint8_t*>(v);
   uint8_t* ob = static_cast<uint8_t*>(ac.o);
-  if (a.plan.n_main > 0)
-    hipLaunchKernelGGL((attn_fwd_kernel<D, KIND, NW, false>), dim3((unsigned)a.plan.n_main),
-                       dim3(T::NT), 0, stream, qb, kb, vb, ob, ac.lse, q_scale, k_scale, v_scale,
-                       part, cnt, a);
-  if (a.plan.n_tail > 0)
-    hipLaunchKernelGGL((attn_fwd_kernel<D, KIND, NW, true>), dim3((unsigned)a.plan.G),
-                       dim3(T::NT), 0, stream, qb, kb, vb, ob, ac.lse, q_scale, k_scale, v_scale,
-                       part, cnt, a);
+  auto attend = [&](auto vt_c) {
+    constexpr bool VT = decltype(vt_c)::value;
+    if (a.plan.n_main > 0)
+      hipLaunchKernelGGL((attn_fwd_kernel<D, KIND, NW, false, VT>), dim3((unsigned)a.plan.n_main),
+                         dim3(T::NT), 0, stream, qb, kb, vb, ob, ac.lse, q_scale, k_scale, v_scale,
+                         part, cnt, a);
+    if (a.plan.n_tail > 0)
+      hipLaunchKernelGGL((attn_fwd_kernel<D, KIND, NW, true, VT>), dim3((unsigned)a.plan.G),
+                         dim3(T::NT), 0, stream, qb, kb, vb, ob, ac.lse, q_scale, k_scale, v_scale,
+                         part, cnt, a);
+  };
+  if constexpr (D == 128 && KIND == kBF16) {
+    if (ac.vt != nullptr) {
+      // long sequences: V read through its V^T tiles (one 16-byte LDS read per product operand)
+      hipLaunchKernelGGL(vt_tiles_kernel, dim3((unsigned)((long long)ac.B * ac.H * nkt)), dim3(256),
+                         0, stream, static_cast<const uint16_t*>(v), vs, ac.H, ac.S, nkt,
+                         static_cast<uint16_t*>(ac.vt));
+      vb = static_cast<const uint8_t*>(ac.vt);
+      attend(std::true_type{});
+      return hipGetLastError();
+    }
+  }
+  attend(std::false_type{});
   return hipGetLastError();
 }
 
 }  // namespace
+
+size_t attn_vt_bytes(int B, int H, int S, int D) {
+  if (D != 128 || S < kVtMinS) return 0;
+  return (size_t)B * H * ((S + kBK - 1) / kBK) * (size_t)(128 * kBK * 2);
+}
 
 size_t attn_tail_bytes(int S, int D) {
   const int nkt = (S + kBK - 1) / kBK;

@@ -84,7 +84,13 @@ ditattn::AttnCall make_call(const void* q, const void* k, const void* v, void* o
   ac.B = B; ac.H = H; ac.S = S; ac.D = D; ac.scale = scale;
   ac.Sq = S;
   ac.tail = nullptr;
+  ac.vt = nullptr;
   return ac;
+}
+
+// The bf16 call's workspace: the tail area, then (long sequences) the V^T tiles.
+size_t attn_bf16_scratch_bytes(int B, int H, int S, int D) {
+  return align_up(ditattn::attn_tail_bytes(S, D), kSegAlign) + ditattn::attn_vt_bytes(B, H, S, D);
 }
 
 void contiguous_strides(int H, int S, int D, int64_t st[12]) {
@@ -189,7 +195,7 @@ int attn_fwd_bf16_ex(const void* q, const void* k, const void* v, void* o, int o
 
 size_t attn_bf16_workspace_bytes(int B, int H, int S, int D) {
   if (check_attn_shape(B, H, S, D) != DITATTN_OK) return 0;
-  return std::max(ditattn::attn_tail_bytes(S, D), kSegAlign);
+  return std::max(attn_bf16_scratch_bytes(B, H, S, D), kSegAlign);
 }
 
 int attn_fwd_bf16_ws(const void* q, const void* k, const void* v, void* o, int out_dtype,
@@ -202,7 +208,10 @@ int attn_fwd_bf16_ws(const void* q, const void* k, const void* v, void* o, int o
     return DITATTN_EWORKSPACE;
   ditattn::AttnCall ac =
       make_call(q, k, v, o, out_dtype == DITATTN_OUT_BF16, lse, strides, B, H, S, D, scale);
-  if (ditattn::attn_tail_bytes(S, D) > 0) ac.tail = workspace;
+  uint8_t* const ws = static_cast<uint8_t*>(workspace);
+  const size_t tail = ditattn::attn_tail_bytes(S, D);
+  if (tail > 0) ac.tail = ws;
+  if (ditattn::attn_vt_bytes(B, H, S, D) > 0) ac.vt = ws + align_up(tail, kSegAlign);
   return status_of(ditattn::launch_attn_bf16(ac, static_cast<hipStream_t>(stream)));
 }
 

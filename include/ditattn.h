@@ -179,7 +179,10 @@ DITATTN_API int attn_fwd_bf16_ex(const void* q, const void* k, const void* v, vo
  * maximum and sum: the online softmax of the "Flash Attention 2 for Z-Image S3-DiT" page,
  * method paragraph, applied across parts), in a fixed order, so the output does not depend on
  * timing.  Tiles of the full rounds are computed exactly as attn_fwd_bf16 computes them; in
- * the last round each tile's sums over the keys are formed in parts and then merged.
+ * the last round each tile's sums over the keys are formed in parts and then merged.  At D =
+ * 128 and S >= 32768 the workspace also holds a transposed copy of V in 64-key tiles, written
+ * by the call, from which the PV products read their operand with one LDS read instead of
+ * two; the products are the same (same values, same order), so this changes no output bit.
  *   workspace : device buffer of >= attn_bf16_workspace_bytes(B, H, S, D) bytes, 256-byte
  *               aligned, caller owned, contents unspecified before and after; calls that use
  *               one workspace at the same time (on different streams) race

@@ -111,10 +111,19 @@ def _tail_bytes(S, D):
     return 1024 + 2 * 256 * 512 * (D // 2 + 2) * 4
 
 
-@pytest.mark.parametrize("S", [1, 64, 448, 449, 512, 4608, 11440, 118800])
+def _vt_bytes(B, H, S, D):
+    """V^T tiles of long bf16 calls (D = 128, S >= 32768): per (b, h) one tile of 128 channel
+    rows x 64 bf16 keys per 64-key tile."""
+    if D != 128 or S < 32768:
+        return 0
+    return B * H * math.ceil(S / 64) * 128 * 64 * 2
+
+
+@pytest.mark.parametrize("S", [1, 64, 448, 449, 512, 4608, 11440, 32767, 32768, 33000, 118800])
 @pytest.mark.parametrize("D", [64, 128])
 def test_bf16_workspace_size(L, S, D):
-    assert L.attn_bf16_workspace_bytes(1, 24, S, D) == max(_tail_bytes(S, D), 256)
+    want = max(_align(_tail_bytes(S, D)) + _vt_bytes(1, 24, S, D), 256)
+    assert L.attn_bf16_workspace_bytes(1, 24, S, D) == want
     assert L.attn_bf16_workspace_bytes(1, 24, S, 96) == 0
     assert L.attn_bf16_workspace_bytes(0, 24, S, D) == 0
 

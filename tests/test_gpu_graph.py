@@ -3,10 +3,11 @@
 Every call enqueues only kernels on the caller's stream (no allocation, no memset, no host
 synchronisation), so a step of the path can be captured once and replayed: the bf16 call on
 its workspace (whole rounds, the shared-out last round and, when there is no whole round, the
-kernel that zeroes its arrival counters), the int8-QK call (prepass and attention, the same
-split) and the relative-L1 reduction.  The graph is replayed several times with eager work and
-synchronisations in between and with the outputs cleared before each replay; every replay must
-reproduce the eager results bit for bit (the calls are deterministic).
+kernel that zeroes its arrival counters; for long sequences the V^T tile prepass), the int8-QK
+call (prepass and attention, the same split) and the relative-L1 reduction.  The graph is
+replayed several times with eager work and synchronisations in between and with the outputs
+cleared before each replay; every replay must reproduce the eager results bit for bit (the
+calls are deterministic).
 """
 import sys
 
@@ -33,8 +34,9 @@ def dev(bits):
 
 
 # B1 H5 S4000: 80 tiles, all shared out (no whole round: the zeroing kernel runs);
-# B2 H24 S4608: 864 tiles, three whole rounds and 96 tiles shared out.
-@pytest.mark.parametrize("B,H,S,D", [(1, 5, 4000, 64), (2, 24, 4608, 128)])
+# B2 H24 S4608: 864 tiles, three whole rounds and 96 tiles shared out;
+# B1 H2 S33000: V read through V^T tiles written by their prepass kernel.
+@pytest.mark.parametrize("B,H,S,D", [(1, 5, 4000, 64), (2, 24, 4608, 128), (1, 2, 33000, 128)])
 def test_graph_replay_matches_eager(B, H, S, D):
     announce(f"graph of bf16 + int8-QK + rel-L1, B{B} H{H} S{S} D{D}")
     q = dev(datagen.normal_bf16((B, H, S, D), 1100 + D, 0))
