@@ -41,11 +41,13 @@ SUSTAINED = {}
 # The int8-QK call does half its counted flops (QK) on int8 MFMA and half (PV) on bf16 MFMA, so
 # even at both peaks it reaches only 1 / (0.5 / 5000 + 0.5 / 2500) = 3333 TOPS (66.7% of int8).
 PEAK_INT8_BF16PV_TOPS = 1.0 / (0.5 / PEAK_INT8_TOPS + 0.5 / PEAK_BF16_TFLOPS)
-# The bf16 call on its workspace is two launches of one kernel template: the 43 whole rounds of
-# 256-row query tiles and the last 152 tiles shared out over the CUs.  The roofline covers the
-# call (both launches): its flops over its HIP-event time, its counters summed.
-ATTN_KERNEL = ("attn_fwd_kernel<128, 0, 8, false> + attn_fwd_kernel<128, 0, 8, true> "
-               "(one attn_fwd_bf16_ws call: whole rounds, then the shared-out last round)")
+# The bf16 call on its workspace is three launches at this length: the V^T tiles of V, then two
+# launches of one kernel template, the 43 whole rounds of 256-row query tiles and the last 152
+# tiles shared out over the CUs.  The roofline covers the call (all three launches): its flops
+# over its HIP-event time, its counters summed.
+ATTN_KERNEL = ("vt_tiles_kernel + attn_fwd_kernel<128, 0, 8, false, true> + "
+               "attn_fwd_kernel<128, 0, 8, true, true> (one attn_fwd_bf16_ws call: V^T tiles, "
+               "whole rounds, then the shared-out last round)")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_bf16_longvideo_traffic.json")
 
 
