@@ -22,6 +22,7 @@ import hashlib
 import json
 import math
 import os
+import re
 import sys
 import time
 
@@ -76,10 +77,15 @@ def make_residuals(torch, rows, cols, seed, noise=0.05):
 
 
 def kernel_source_hash():
+    """Hash of the attention kernel's code: its sources with comments removed and whitespace
+    collapsed, so that an edit of comments alone does not invalidate recorded counters."""
     h = hashlib.sha256()
     for name in ("attn_fwd.hip", "device_common.h"):
-        with open(os.path.join(ROOT, "diffusion_transformer_attention_amd", "csrc", name), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, "diffusion_transformer_attention_amd", "csrc", name)) as f:
+            code = f.read()
+        code = re.sub(r"/\*.*?\*/", " ", code, flags=re.S)   # (no string literal holds // or /*)
+        code = re.sub(r"//[^\n]*", " ", code)
+        h.update(" ".join(code.split()).encode())
     return h.hexdigest()[:16]
 
 

@@ -29,7 +29,11 @@
 //   * Software pipeline, three independent streams per stage in one basic block: stage j
 //     computes S[j+2] = K[j+2] Q^T on the matrix cores, turns S[j+1] into the weights P[j+1]
 //     on the VALU, and accumulates O += V[j]^T P[j]; it issues the loads of K[j+3] and V[j+1]
-//     (K runs three tiles ahead of V); one barrier per stage.
+//     (K runs three tiles ahead of V); one barrier per stage.  For bf16 at D = 128 the stage
+//     asks the compiler for its exponential / matrix-product interleave, which spreads the
+//     32 exponentials evenly between the 32 products.
+//   * Long bf16 calls (with a workspace) first copy V into V^T tiles, each 16-key step in the
+//     order the P^T operand holds its keys, so a PV operand is one 16-byte LDS read.
 //   * int8 scores leave the matrix cores already as fp32: the integer accumulator starts at
 //     the bit pattern of 1.5 * 2^23, so its final bits read as fp32 are 1.5 * 2^23 plus the
 //     score, exactly; the bias folds into the exponent offset (no conversion instructions).
@@ -70,7 +74,7 @@ constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kLazyW = 256.0f;  // 2^8: largest weight (and lane weight sum) kept as it is
 // bf16 calls over at least this many keys (D = 128, with a workspace) read V through V^T tiles
 // written by a prepass: one 16-byte LDS read per PV operand instead of two transposing ones,
-// 1-1.6% faster at S = 118800 with the prepass (a read and a write of V) included.  The
+// 1.6-1.9% faster at S = 118800 with the prepass (a read and a write of V) included.  The
 // prepass costs 2% of the call at S = 11440, as much as the tiles save; on the int8-QK kernel
 // the tiles gain nothing.
 constexpr int kVtMinS = 32768;
