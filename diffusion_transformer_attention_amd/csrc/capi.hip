@@ -88,8 +88,8 @@ ditattn::AttnCall make_call(const void* q, const void* k, const void* v, void* o
   return ac;
 }
 
-// The bf16 call's workspace: the tail area, then (long sequences) the V^T tiles.
-size_t attn_bf16_scratch_bytes(int B, int H, int S, int D) {
+// The attention launch's own scratch: the tail area, then (long sequences) the V^T tiles.
+size_t attn_scratch_bytes(int B, int H, int S, int D) {
   return align_up(ditattn::attn_tail_bytes(S, D), kSegAlign) + ditattn::attn_vt_bytes(B, H, S, D);
 }
 
@@ -120,7 +120,11 @@ int q8_run(ditattn::AttnCall ac, Q8Mode mode, void* workspace, size_t workspace_
   int8_t* k_codes = reinterpret_cast<int8_t*>(ws + off[4]);
   double* partial = reinterpret_cast<double*>(ws + off[5]);
   // the scratch segment serves the attention launch too, after the prepass is done with it
-  if (ditattn::attn_tail_bytes(ac.S, ac.D) > 0) ac.tail = ws + off[5];
+  // (V^T tiles for the int8-QK kind only: on the fp8 kinds they were not measured to pay)
+  const size_t tail = ditattn::attn_tail_bytes(ac.S, ac.D);
+  if (tail > 0) ac.tail = ws + off[5];
+  if (mode == kQ8Int8 && ditattn::attn_vt_bytes(ac.B, ac.H, ac.S, ac.D) > 0)
+    ac.vt = ws + off[5] + align_up(tail, kSegAlign);
   const hipError_t e = ditattn::launch_prepass(ac.q, ac.qs, ac.k, ac.ks, k_mean, partial, q_codes,
                                                k_codes, q_scale, k_scale, ac.B, ac.H, ac.S, ac.D,
                                                fp8, s);
@@ -195,7 +199,7 @@ int attn_fwd_bf16_ex(const void* q, const void* k, const void* v, void* o, int o
 
 size_t attn_bf16_workspace_bytes(int B, int H, int S, int D) {
   if (check_attn_shape(B, H, S, D) != DITATTN_OK) return 0;
-  return std::max(attn_bf16_scratch_bytes(B, H, S, D), kSegAlign);
+  return std::max(attn_scratch_bytes(B, H, S, D), kSegAlign);
 }
 
 int attn_fwd_bf16_ws(const void* q, const void* k, const void* v, void* o, int out_dtype,
@@ -224,9 +228,9 @@ size_t attn_int8qk_workspace_offsets(int B, int H, int S, int D, size_t offsets[
       bh * (size_t)((S + 63) / 64) * sizeof(float),         // k_scale
       bh * (size_t)S * D,                                   // q_codes
       bh * (size_t)S * D,                                   // k_codes
-      // mean partials, then (once the codes are formed) the attention's tail workspace
+      // mean partials, then (once the codes are formed) the attention's scratch
       std::max(bh * (size_t)ditattn::kmean_chunks(B, H, S) * D * 2 * sizeof(double),
-               ditattn::attn_tail_bytes(S, D)),
+               attn_scratch_bytes(B, H, S, D)),
   };
   size_t off = 0;
   for (int i = 0; i < 6; ++i) {

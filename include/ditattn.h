@@ -78,7 +78,8 @@ DITATTN_API int attn_fwd_bf16(const void* q, const void* k, const void* v, float
  *   [3] q_codes int8 [B, H, S, D]
  *   [4] k_codes int8 [B, H, S, D]
  *   [5] scratch  fp64 pairs used while forming k_mean, then the attention's tail workspace
- *                (see attn_fwd_bf16_ws; contents unspecified)
+ *                and, at D = 128 and S >= 32768, the V^T tiles of V (see attn_fwd_bf16_ws;
+ *                contents unspecified)
  * After a successful call segments [0]-[4] hold the values the attention used. */
 DITATTN_API size_t attn_int8qk_workspace_bytes(int B, int H, int S, int D);
 

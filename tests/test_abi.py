@@ -71,8 +71,8 @@ def test_int8_workspace_layout(L, B, H, S, D):
         assert off[i] == expect and off[i] % 256 == 0
         expect = _align(expect + sz)
     assert off[5] == expect and total > off[5] and total % 256 == 0
-    # the scratch segment also holds the attention's tail workspace
-    assert total - off[5] >= _tail_bytes(S, D)
+    # the scratch segment also holds the attention's tail workspace and V^T tiles
+    assert total - off[5] >= _align(_tail_bytes(S, D)) + _vt_bytes(B, H, S, D)
 
 
 @pytest.mark.parametrize("B,H,S,D", [(1, 2, 256, 128), (1, 24, 118800, 128), (3, 1, 1, 128)])
@@ -112,8 +112,8 @@ def _tail_bytes(S, D):
 
 
 def _vt_bytes(B, H, S, D):
-    """V^T tiles of long bf16 calls (D = 128, S >= 32768): per (b, h) one tile of 128 channel
-    rows x 64 bf16 keys per 64-key tile."""
+    """V^T tiles of long bf16 and int8-QK calls (D = 128, S >= 32768): per (b, h) one tile of
+    128 channel rows x 64 bf16 keys per 64-key tile."""
     if D != 128 or S < 32768:
         return 0
     return B * H * math.ceil(S / 64) * 128 * 64 * 2

@@ -1,4 +1,5 @@
-"""GPU: long bf16 calls read V through V^T tiles (S >= 32768 at D = 128, with a workspace).
+"""GPU: long bf16 and int8-QK calls read V through V^T tiles (S >= 32768 at D = 128, with a
+workspace).
 
 The tiles are written by a prepass (64 keys of 128 channels each, every 16-key step in the key
 order of the weights operand), and the attention reads each PV operand with one 16-byte LDS
@@ -11,7 +12,9 @@ read instead of two transposing ones.  The products see the same values in the s
   contiguous one;
 * with a shared-out last round (B1 H24 S33000) the output is checked against the oracle on
   sampled rows of every head, at the bars of test_gpu_parity.py, and repeated calls from a
-  garbage workspace are bit-identical.
+  garbage workspace are bit-identical;
+* the int8-QK call (always on a workspace) is checked on sampled rows against the oracle's
+  attention on the same codes, and its codes bit-exact, as in test_gpu_parity.py.
 The ragged length (33000 = 515 * 64 + 40) puts the last key tile on the final 64 rows, as the
 K tile, with the keys it shares with the previous tile masked.
 """
@@ -32,6 +35,7 @@ if not torch.cuda.is_available():
 import diffusion_transformer_attention_amd as dta  # noqa: E402
 
 BF16_MAXABS, BF16_RELL2 = 2e-2, 5e-3
+INT8_RELL2 = 1e-2
 S_LONG = 33000
 
 
@@ -119,3 +123,27 @@ def test_vt_with_shared_out_round_sampled():
     err, r = np.abs(got - ref).max(), rel_l2(got, ref)
     announce(f"  {rows.size} rows per head: max-abs {err:.3e} rel-L2 {r:.3e}")
     assert err <= BF16_MAXABS and r <= BF16_RELL2, (err, r)
+
+
+def test_vt_int8_sampled():
+    B, H, S, D = 1, 2, S_LONG, 128
+    announce(f"attn_fwd_int8qk B{B} H{H} S{S} D{D} through V^T tiles")
+    q, k, v = inputs(B, H, S, D, 1230)
+    ws = dta.int8qk_workspace(B, H, S, D, "cuda")
+    ws.fill_(0xFF)
+    out = dta.attn_fwd_int8qk(dev(q), dev(k), dev(v), workspace=ws)
+    torch.cuda.synchronize()
+    views = {n: t.cpu().numpy() for n, t in dta.int8qk_views(ws, B, H, S, D).items()}
+    rows = datagen.sample_rows(S, 256, seed=79)
+    got = out.index_select(2, torch.from_numpy(rows).cuda()).cpu().numpy()
+    ref = oracle.quantize_qk(f64(q), f64(k))
+    for key in ("q_codes", "k_codes"):
+        assert int(np.sum(views[key] != ref[key])) == 0, key
+    for key in ("k_mean", "q_scale", "k_scale"):
+        assert int(np.sum(views[key].view(np.uint32) != ref[key].view(np.uint32))) == 0, key
+    oq = oracle.attention_int8(ref["q_codes"], ref["q_scale"], ref["k_codes"], ref["k_scale"],
+                               f64(v), rows=rows)
+    r = rel_l2(got, oq)
+    announce(f"  codes bit-exact; {rows.size} rows per head: rel-L2 vs the oracle on the same codes {r:.3e}")
+    assert np.all(np.isfinite(got))
+    assert r <= INT8_RELL2, r
