@@ -32,8 +32,8 @@
 //     (K runs three tiles ahead of V); one barrier per stage.  For bf16 at D = 128 the stage
 //     asks the compiler for its exponential / matrix-product interleave, which spreads the
 //     32 exponentials evenly between the 32 products.
-//   * Long bf16 and int8-QK calls (with a workspace) first copy V into V^T tiles, each 16-key
-//     step in the order the P^T operand holds its keys, so a PV operand is one 16-byte LDS read.
+//   * Long calls with bf16 V (and a workspace) first copy V into V^T tiles, each 16-key step in
+//     the order the P^T operand holds its keys, so a PV operand is one 16-byte LDS read.
 //   * int8 scores leave the matrix cores already as fp32: the integer accumulator starts at
 //     the bit pattern of 1.5 * 2^23, so its final bits read as fp32 are 1.5 * 2^23 plus the
 //     score, exactly; the bias folds into the exponent offset (no conversion instructions).
@@ -72,9 +72,9 @@ constexpr int kBK = 64;         // keys per tile (= int8 K block)
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kLazyW = 256.0f;  // 2^8: largest weight (and lane weight sum) kept as it is
-// bf16 and int8-QK calls over at least this many keys (D = 128, with a workspace) read V
-// through V^T tiles written by a prepass: one 16-byte LDS read per PV operand instead of two
-// transposing ones, 1.6-1.9% faster at S = 118800 on either kind with the prepass (a read and a
+// Calls with bf16 V over at least this many keys (D = 128, with a workspace) read V through V^T
+// tiles written by a prepass: one 16-byte LDS read per PV operand instead of two transposing
+// ones, 1.5-2% faster at S = 118800 (bf16, int8-QK, fp8-QK) with the prepass (a read and a
 // write of V) included.  The prepass costs 2% of the bf16 call at S = 11440, as much as the
 // tiles save there.
 constexpr int kVtMinS = 32768;
@@ -184,7 +184,7 @@ struct KArgs {
 // the design and a third wave slot could not hold a second workgroup, yet aiming for three
 // squeezes the kernel into 168 VGPRs and serialises its K fragment reads behind the products.
 // (At D = 128 the cap changes nothing but the instruction schedule, measurably for the worse.)
-// VT: vp holds the V^T tiles of vt_tiles_kernel (bf16 and int8-QK kinds, D = 128) instead of V.
+// VT: vp holds the V^T tiles of vt_tiles_kernel (the kinds with bf16 V, D = 128) instead of V.
 template <int D, int KIND, int NW, bool TAIL, bool VT>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, D == 64 ? 2 : 8)))
 void attn_fwd_kernel(const uint8_t* __restrict__ qp, const uint8_t* __restrict__ kp,
@@ -199,7 +199,7 @@ void attn_fwd_kernel(const uint8_t* __restrict__ qp, const uint8_t* __restrict__
   constexpr bool F8 = KIND == kFp8 || KIND == kFp8All;
   constexpr bool V8 = KIND == kFp8All;  // fp8 V codes, PV on the fp8 matrix cores
   static_assert(!V8 || D == 128, "fp8 V is laid out for D = 128");
-  static_assert(!VT || (D == 128 && (KIND == kBF16 || KIND == kInt8)), "V^T tiles: bf16 V, D = 128");
+  static_assert(!VT || (D == 128 && !V8), "V^T tiles: bf16 V, D = 128");
   using T = Tile<D, INT8, NW, V8>;
   constexpr int EBV = V8 ? 1 : 2;       // bytes per V element
   constexpr int kThreads = T::NT;
@@ -607,10 +607,11 @@ void attn_fwd_kernel(const uint8_t* __restrict__ qp, const uint8_t* __restrict__
       if (j + 1 < kend) load_v(j + 1, vb_next);
 
       // bf16 at D = 128: the compiler's interleave of exponentials with matrix products for
-      // this block (2-3% faster; the 8-bit kinds and D = 64 run slower with it).  int8-QK on V^T
-      // tiles: its interleave of LDS reads with products (1.5-1.9%; slower without the tiles).
+      // this block (2-3% faster; the 8-bit kinds and D = 64 run slower with it).  8-bit QK on
+      // V^T tiles: its interleave of LDS reads with products (with the tiles 1.5-1.9% faster on
+      // int8-QK and 1.6% on fp8-QK than reading V as it is; on int8-QK it loses without them).
       if constexpr (KIND == kBF16 && D == 128) __builtin_amdgcn_iglp_opt(3);
-      if constexpr (KIND == kInt8 && D == 128 && VT) __builtin_amdgcn_iglp_opt(0);
+      if constexpr ((KIND == kInt8 || KIND == kFp8) && D == 128 && VT) __builtin_amdgcn_iglp_opt(0);
       // (past the last tile these compute on stale data and are discarded)
       qk(kb_read, s2);
       float lt, cf;
@@ -990,7 +991,7 @@ hipError_t launch(const AttnCall& ac, const void* q, Strides qs, const void* k, 
                          dim3(T::NT), 0, stream, qb, kb, vb, ob, ac.lse, q_scale, k_scale, v_scale,
                          part, cnt, a);
   };
-  if constexpr (D == 128 && (KIND == kBF16 || KIND == kInt8)) {
+  if constexpr (D == 128 && KIND != kFp8All) {
     if (ac.vt != nullptr) {
       // long sequences: V read through its V^T tiles (one 16-byte LDS read per product operand)
       hipLaunchKernelGGL(vt_tiles_kernel, dim3((unsigned)((long long)ac.B * ac.H * nkt)), dim3(256),

@@ -120,10 +120,10 @@ int q8_run(ditattn::AttnCall ac, Q8Mode mode, void* workspace, size_t workspace_
   int8_t* k_codes = reinterpret_cast<int8_t*>(ws + off[4]);
   double* partial = reinterpret_cast<double*>(ws + off[5]);
   // the scratch segment serves the attention launch too, after the prepass is done with it
-  // (V^T tiles for the int8-QK kind only: on the fp8 kinds they were not measured to pay)
+  // (V^T tiles when V is bf16: not for fp8 for both products, which reads V codes)
   const size_t tail = ditattn::attn_tail_bytes(ac.S, ac.D);
   if (tail > 0) ac.tail = ws + off[5];
-  if (mode == kQ8Int8 && ditattn::attn_vt_bytes(ac.B, ac.H, ac.S, ac.D) > 0)
+  if (mode != kQ8Fp8All && ditattn::attn_vt_bytes(ac.B, ac.H, ac.S, ac.D) > 0)
     ac.vt = ws + off[5] + align_up(tail, kSegAlign);
   const hipError_t e = ditattn::launch_prepass(ac.q, ac.qs, ac.k, ac.ks, k_mean, partial, q_codes,
                                                k_codes, q_scale, k_scale, ac.B, ac.H, ac.S, ac.D,

@@ -35,7 +35,7 @@ struct AttnCall {
   // its last, partly filled round of query tiles out over every CU; null: whole tiles only.
   void* tail;
   // attn_vt_bytes(B, H, S, D) bytes (256-byte aligned, apart from `tail`) for the V^T tiles a
-  // long bf16 or int8-QK launch reads V through; null: V read as it is (always for fp8).
+  // long launch with bf16 V reads V through; null: V read as it is.
   void* vt;
 };
 
@@ -43,8 +43,8 @@ struct AttnCall {
 // can have a tail phase).
 size_t attn_tail_bytes(int S, int D);
 
-// Bytes of the V^T tiles of a bf16 or int8-QK launch over [B, H, S, D] (0 when it reads V as it
-// is: D = 64, or S below the length from which the tiles pay).
+// Bytes of the V^T tiles of a launch with bf16 V over [B, H, S, D] (0 when it reads V as it is:
+// D = 64, or S below the length from which the tiles pay).
 size_t attn_vt_bytes(int B, int H, int S, int D);
 
 hipError_t launch_attn_bf16(const AttnCall& ac, hipStream_t stream);

@@ -1,5 +1,5 @@
-"""GPU: long bf16 and int8-QK calls read V through V^T tiles (S >= 32768 at D = 128, with a
-workspace).
+"""GPU: long calls with bf16 V read V through V^T tiles (S >= 32768 at D = 128, with a
+workspace): bf16, int8-QK and fp8-QK attention.
 
 The tiles are written by a prepass (64 keys of 128 channels each, every 16-key step in the key
 order of the weights operand), and the attention reads each PV operand with one 16-byte LDS
@@ -13,8 +13,9 @@ read instead of two transposing ones.  The products see the same values in the s
 * with a shared-out last round (B1 H24 S33000) the output is checked against the oracle on
   sampled rows of every head, at the bars of test_gpu_parity.py, and repeated calls from a
   garbage workspace are bit-identical;
-* the int8-QK call (always on a workspace) is checked on sampled rows against the oracle's
-  attention on the same codes, and its codes bit-exact, as in test_gpu_parity.py.
+* the int8-QK and fp8-QK calls (always on a workspace) are checked on sampled rows against the
+  oracle's attention on the same codes, and their codes bit-exact, as in test_gpu_parity.py and
+  test_gpu_fp8.py.
 The ragged length (33000 = 515 * 64 + 40) puts the last key tile on the final 64 rows, as the
 K tile, with the keys it shares with the previous tile masked.
 """
@@ -125,24 +126,29 @@ def test_vt_with_shared_out_round_sampled():
     assert err <= BF16_MAXABS and r <= BF16_RELL2, (err, r)
 
 
-def test_vt_int8_sampled():
+@pytest.mark.parametrize("kind", ["int8", "fp8"])
+def test_vt_8bit_sampled(kind):
     B, H, S, D = 1, 2, S_LONG, 128
-    announce(f"attn_fwd_int8qk B{B} H{H} S{S} D{D} through V^T tiles")
+    announce(f"attn_fwd_{kind}qk B{B} H{H} S{S} D{D} through V^T tiles")
     q, k, v = inputs(B, H, S, D, 1230)
     ws = dta.int8qk_workspace(B, H, S, D, "cuda")
     ws.fill_(0xFF)
-    out = dta.attn_fwd_int8qk(dev(q), dev(k), dev(v), workspace=ws)
+    fn = dta.attn_fwd_int8qk if kind == "int8" else dta.attn_fwd_fp8qk
+    out = fn(dev(q), dev(k), dev(v), workspace=ws)
     torch.cuda.synchronize()
     views = {n: t.cpu().numpy() for n, t in dta.int8qk_views(ws, B, H, S, D).items()}
+    if kind == "fp8":  # e4m3 bytes
+        for n in ("q_codes", "k_codes"):
+            views[n] = views[n].view(np.uint8)
     rows = datagen.sample_rows(S, 256, seed=79)
     got = out.index_select(2, torch.from_numpy(rows).cuda()).cpu().numpy()
-    ref = oracle.quantize_qk(f64(q), f64(k))
+    ref = (oracle.quantize_qk if kind == "int8" else oracle.quantize_qk_fp8)(f64(q), f64(k))
     for key in ("q_codes", "k_codes"):
         assert int(np.sum(views[key] != ref[key])) == 0, key
     for key in ("k_mean", "q_scale", "k_scale"):
         assert int(np.sum(views[key].view(np.uint32) != ref[key].view(np.uint32))) == 0, key
-    oq = oracle.attention_int8(ref["q_codes"], ref["q_scale"], ref["k_codes"], ref["k_scale"],
-                               f64(v), rows=rows)
+    attend = oracle.attention_int8 if kind == "int8" else oracle.attention_fp8
+    oq = attend(ref["q_codes"], ref["q_scale"], ref["k_codes"], ref["k_scale"], f64(v), rows=rows)
     r = rel_l2(got, oq)
     announce(f"  codes bit-exact; {rows.size} rows per head: rel-L2 vs the oracle on the same codes {r:.3e}")
     assert np.all(np.isfinite(got))
