@@ -9,7 +9,8 @@ read instead of two transposing ones.  The products see the same values in the s
   to split), the workspace call through the tiles is bit-identical to the plain call, which
   reads V as it is; both are also checked against the fp64 oracle on every row;
 * a strided V (interleaved heads) gives the same tiles and the same output bits as the
-  contiguous one;
+  contiguous one and as the plain call, with one batch of two heads and with two batches of one
+  head;
 * with a shared-out last round (B1 H24 S33000) the output is checked against the oracle on
   sampled rows of every head, at the bars of test_gpu_parity.py, and repeated calls from a
   garbage workspace are bit-identical;
@@ -88,16 +89,19 @@ def test_vt_bf16_bit_identical_and_every_row():
     assert err <= BF16_MAXABS and r <= BF16_RELL2, (err, r)
 
 
-def test_vt_strided_v_same_bits():
-    B, H, S, D = 1, 2, S_LONG, 128
+@pytest.mark.parametrize("B,H", [(1, 2), (2, 1)])
+def test_vt_strided_v_same_bits(B, H):
+    S, D = S_LONG, 128
     announce(f"bf16 B{B} H{H} S{S} D{D}: [B, S, H, D] views through V^T tiles")
     q, k, v = (dev(x) for x in inputs(B, H, S, D, 1210))
     ref = dta.attn_fwd_bf16(q, k, v)
+    plain = dta.attn_fwd_bf16(q, k, v, workspace=False)  # V as it is (258 tiles: no split either)
     tq, tk, tv = (x.transpose(1, 2).contiguous().transpose(1, 2) for x in (q, k, v))
     got = dta.attn_fwd_bf16(tq, tk, tv)
     torch.cuda.synchronize()
     assert torch.equal(got, ref)
-    announce("  bit-identical to the contiguous call")
+    assert torch.equal(ref, plain)
+    announce("  bit-identical to the contiguous call and to the call that reads V as it is")
 
 
 def test_vt_with_shared_out_round_sampled():
