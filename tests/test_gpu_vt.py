@@ -11,6 +11,7 @@ read instead of two transposing ones.  The products see the same values in the s
 * a strided V (interleaved heads) gives the same tiles and the same output bits as the
   contiguous one and as the plain call, with one batch of two heads and with two batches of one
   head;
+* the bf16 output and the log-sum-exp through the tiles are bit-identical to the plain call's;
 * with a shared-out last round (B1 H24 S33000) the output is checked against the oracle on
   sampled rows of every head, at the bars of test_gpu_parity.py, and repeated calls from a
   garbage workspace are bit-identical;
@@ -102,6 +103,20 @@ def test_vt_strided_v_same_bits(B, H):
     assert torch.equal(got, ref)
     assert torch.equal(ref, plain)
     announce("  bit-identical to the contiguous call and to the call that reads V as it is")
+
+
+def test_vt_bf16_output_and_lse_same_bits():
+    """bf16 output and the per-row log-sum-exp through the V^T tiles: bit-identical to the plain
+    call (B1 H2 S33000 has no shared-out round)."""
+    B, H, S, D = 1, 2, S_LONG, 128
+    announce(f"bf16 B{B} H{H} S{S} D{D}: bf16 output and lse through V^T tiles")
+    q, k, v = (dev(x) for x in inputs(B, H, S, D, 1215))
+    o1, l1 = dta.attn_fwd_bf16(q, k, v, out_dtype=torch.bfloat16, lse=True)
+    o2, l2 = dta.attn_fwd_bf16(q, k, v, out_dtype=torch.bfloat16, lse=True, workspace=False)
+    torch.cuda.synchronize()
+    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
+    assert torch.equal(l1, l2)
+    announce("  bf16 output and lse bit-identical to the plain call")
 
 
 def test_vt_with_shared_out_round_sampled():
